@@ -1,0 +1,85 @@
+"""NumPy fp64 forms of the KDA recurrence (test infrastructure only).
+
+seq      the per-token sequential definition, step by step:
+           g <- clamp(g, -5, 0); P = Diag(e^g) S; u = beta (v - P^T k);
+           S = P + k u^T; o = S^T q.
+         Decay floor of -5: "K3 tech report" transcript (the exchange on the
+         lower log-decay bound) and "Kimi K3 goes trillion-scale ..." subtitles,
+         cue 14. Delta rule with channel-wise forget gate and a fixed-size state:
+         "177: Kimi K3 in Detail", section 15; same subtitles, cue 14.
+
+chunked  the same result reached chunk by chunk, written out matrix by matrix
+         from the chunk form obtained by unrolling the recurrence over a chunk
+         of C tokens (the 16-token tile of the "K3 tech report" transcript):
+           Gamma_r = sum_{s<=r} g_s (per key channel), gamma = Gamma_C
+           Qt = e^Gamma * Q, Kt = e^Gamma * K, Kh = e^-Gamma * K, Kb = e^(gamma-Gamma) * K
+           A = strictly_lower(diag(beta) Kt Kh^T),  M = lower_incl(Qt Kh^T)
+           Tm = (I + A)^-1,  W = Tm diag(beta) Kt,  Ut = Tm diag(beta) V
+           U = Ut - W S0,  O = Qt S0 + M U,  S_C = Diag(e^gamma) S0 + Kb^T U
+         A last chunk shorter than C is just a shorter chunk.
+
+Arrays are per (batch, head): q, k, g [T, dk]; v [T, dv]; beta [T]; S0 [dk, dv].
+All arithmetic is float64.
+"""
+import numpy as np
+
+
+def clamp_decay(g):
+    """Clamp log-decay to [-5, 0]; NaN stays NaN (np.clip propagates NaN)."""
+    return np.clip(np.asarray(g, np.float64), -5.0, 0.0)
+
+
+def seq(q, k, v, g, beta, S0=None):
+    q, k, v, beta = (np.asarray(x, np.float64) for x in (q, k, v, beta))
+    g = clamp_decay(g)
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, np.float64, copy=True)
+    o = np.empty((T, dv))
+    for t in range(T):
+        P = np.exp(g[t])[:, None] * S
+        u = beta[t] * (v[t] - P.T @ k[t])
+        S = P + np.outer(k[t], u)
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def chunked(q, k, v, g, beta, S0=None, C=16):
+    q, k, v, beta = (np.asarray(x, np.float64) for x in (q, k, v, beta))
+    g = clamp_decay(g)
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, np.float64, copy=True)
+    o = np.empty((T, dv))
+    for start in range(0, T, C):
+        sl = slice(start, min(start + C, T))
+        n = sl.stop - sl.start
+        Gam = np.cumsum(g[sl], axis=0)
+        gam = Gam[-1]
+        Qt = np.exp(Gam) * q[sl]
+        Kt = np.exp(Gam) * k[sl]
+        Kh = np.exp(-Gam) * k[sl]
+        Kb = np.exp(gam[None, :] - Gam) * k[sl]
+        A = np.tril(beta[sl][:, None] * (Kt @ Kh.T), -1)
+        M = np.tril(Qt @ Kh.T)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        W = Tm @ (beta[sl][:, None] * Kt)
+        Ut = Tm @ (beta[sl][:, None] * v[sl])
+        U = Ut - W @ S
+        o[sl] = Qt @ S + M @ U
+        S = np.exp(gam)[:, None] * S + Kb.T @ U
+    return o, S
+
+
+def seq_batched(q, k, v, g, beta, S0=None, fn=seq, **kw):
+    """Apply a per-(b,h) form to [B,T,H,d]-laid-out arrays."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.empty((B, T, H, dv))
+    ST = np.empty((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            s0 = None if S0 is None else S0[b, h]
+            o[b, :, h], ST[b, h] = fn(q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h],
+                                      beta[b, :, h], s0, **kw)
+    return o, ST

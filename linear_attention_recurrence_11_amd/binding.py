@@ -1,0 +1,140 @@
+"""Thin Python binding of libkda.so (ctypes), same names as the C ABI.
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream, every step of the computation runs in the library's HIP kernels. The
+library is loaded from this package directory on first use; if it is missing
+the call raises (there is no fallback path).
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS_OK = 0
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, _status_text(status), status))
+
+
+def library_path():
+    return os.path.join(_PKG, "libkda.so")
+
+
+def _load():
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                "libkda.so is not built at %s; run `python -m linear_attention_recurrence_11_amd.build`"
+                % path)
+        lib = ctypes.CDLL(path)
+        vp, i64, i, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        lib.kda_abi_version.restype = i
+        lib.kda_abi_version.argtypes = []
+        lib.kda_status_str.restype = ctypes.c_char_p
+        lib.kda_status_str.argtypes = [i]
+        lib.kda_chunk_fwd_workspace_size.restype = sz
+        lib.kda_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i]
+        lib.kda_chunk_fwd.restype = i
+        lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i64] * 5 + [i, i, vp, sz, vp]
+        lib.kda_chunk_fwd_check.restype = i
+        lib.kda_chunk_fwd_check.argtypes = [vp] * 8 + [i64] * 5 + [i, i, vp, sz]
+        lib.kda_decode_step.restype = i
+        lib.kda_decode_step.argtypes = [vp] * 7 + [i64] * 4 + [i, i, vp]
+        lib.kda_decode_step_check.restype = i
+        lib.kda_decode_step_check.argtypes = [vp] * 7 + [i64] * 4 + [i, i]
+        _LIB = lib
+    return _LIB
+
+
+def _status_text(status):
+    try:
+        return _load().kda_status_str(int(status)).decode()
+    except Exception:
+        return "status"
+
+
+def _dcode(dtype):
+    if dtype == torch.float32:
+        return KDA_F32
+    if dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError("KDA tensors must be float32 or bfloat16, got %s" % dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("KDA tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else ctypes.c_void_p(0)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def kda_abi_version():
+    return int(_load().kda_abi_version())
+
+
+def kda_status_str(status):
+    return _load().kda_status_str(int(status)).decode()
+
+
+def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype):
+    code = in_dtype if isinstance(in_dtype, int) else _dcode(in_dtype)
+    return int(_load().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, out_dtype=torch.float32,
+                  want_state=True, workspace=None, stream=None):
+    """Chunkwise KDA forward. q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]
+    (all float32 or all bfloat16, on one GPU); S0 [B,H,dk,dv] float32 or None.
+    Returns (o [B,T,H,dv] out_dtype, S_T [B,H,dk,dv] float32 or None).
+    Pass S_T=S0 to update the state in place."""
+    lib = _load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dcode(q.dtype)
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                           _ptr(S_T), B, T, H, dk, dv, code, _dcode(o.dtype), _ptr(workspace),
+                           wbytes, _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, S_T
+
+
+def kda_decode_step(q, k, v, g, beta, S, *, o=None, out_dtype=torch.float32, stream=None):
+    """One decode step for N requests. q, k, g [N,H,dk]; v [N,H,dv]; beta [N,H];
+    S [N,H,dk,dv] float32, updated in place. Returns o [N,H,dv]."""
+    lib = _load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                             N, H, dk, dv, _dcode(q.dtype), _dcode(o.dtype),
+                             _stream(stream, q.device))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_decode_step")
+    return o

@@ -1,0 +1,525 @@
+// Chunkwise forward of Kimi Delta Attention (KDA) on gfx950.
+//
+// The recurrence (per batch b, head h; state S is dk x dv, fp32):
+//   S_t = (I - beta_t k_t k_t^T) Diag(e^{g_t}) S_{t-1} + beta_t k_t v_t^T,
+//   o_t = S_t^T q_t,   g_t clamped to [-5, 0],
+// is evaluated 16 tokens at a time. Unrolling it over a chunk with entering
+// state S0 (r, s index tokens of the chunk, Gamma_r the inclusive per-channel
+// sum of g up to r, gamma = Gamma_16):
+//   Qt = e^Gamma Q,  Kt = e^Gamma K,  Kh = e^-Gamma K,  Kb = e^(gamma - Gamma) K
+//   A  = strictly_lower(diag(beta) Kt Kh^T),   M = lower_incl(Qt Kh^T)
+//   Tm = (I + A)^-1,   W = Tm diag(beta) Kt,   Ut = Tm diag(beta) V
+//   U  = Ut - W S0,    O = Qt S0 + M U,        S_16 = Diag(e^gamma) S0 + Kb^T U
+// Only the last line couples chunks. The -5 floor keeps e^-Gamma <= e^80 over
+// 16 tokens, inside bf16 range, so the diagonal (intra-chunk) products run as
+// dense matrix-core tiles with no position-by-position path ("K3 tech report"
+// podcast transcript, the exchange on the decay bound; "Kimi K3 goes
+// trillion-scale with sparse MoE efficiency" subtitles, cue 14).
+//
+// Two kernels:
+//  kda_chunk_prep   one wavefront per (b, h, chunk), all chunks in parallel:
+//                   decay scan with DPP row scans (a 16-lane row = the 16
+//                   tokens of a chunk), scaled operands, Gram tiles A and M on
+//                   the matrix cores, (I + A)^-1 by forward substitution in
+//                   LDS, W on the matrix cores; writes one workspace record
+//                   per chunk in matrix-core fragment order.
+//  kda_state_pass   one wavefront per (b, h, 16-column slice of dv): keeps its
+//                   dk x 16 slice of S in registers for the whole sequence and
+//                   applies the last two lines chunk after chunk. Columns of S
+//                   never interact, so slices need no communication.
+//
+// Lane conventions (l = lane, c16 = l % 16, gq = l / 16): a 16x16 MFMA output
+// tile has lane l holding rows 4*gq + i (i = 0..3) of column c16. In the prep
+// kernel lane l owns token c16 and key channels 16*m + 4*gq + i of it; the
+// contraction slots of every dk-contraction are mapped to channels so that the
+// state slice, held in output layout, is directly the B operand of W S and
+// Qt S (no shuffles on the sequential path).
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename InT>
+struct Path {
+  static constexpr bool kF32 = std::is_same<InT, float>::value;
+  // element type of the state-pass matrix operands
+  using Op = typename std::conditional<kF32, float, _Float16>::type;
+};
+
+// ---------------------------------------------------------------------------
+// Record fragment addressing (see RecordLayout). Each lane's values come in
+// groups of 4 consecutive rows/tokens i = 0..3.
+//   W, Q: value (m, i) = X[token c16][channel 16m + 4gq + i]
+//   Kb:   value (m, i) = Kb[token 4gq + i][channel 16m + c16]
+//   M:    value i      = M[c16][4gq + i]
+//   Tb:   value i      = Tm[c16][4gq + i] * beta_{4gq + i}
+//   eg:   e^gamma[channel 16m + 4gq + i] at float index gq*dk/4 + 4m + i
+// fp16 path: W, Q packed per pair of tiles (2p, 2p+1) as 8 halves (16 B) at
+// ((p*64 + l) * 16); Kb as 4 halves at ((m*64 + l) * 8); M as hi then lo
+// halves (l*8 and 512 + l*8); Tb at l*8.
+// fp32 path: W, Q as 4 floats at ((m*64 + l) * 16); Kb likewise; M, Tb at l*16.
+// ---------------------------------------------------------------------------
+
+template <typename InT, int DK>
+__global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
+                                                     const InT* __restrict__ k,
+                                                     const InT* __restrict__ g,
+                                                     const InT* __restrict__ beta,
+                                                     uint8_t* __restrict__ ws, int64_t T,
+                                                     int64_t H, int64_t NC, RecordLayout L) {
+  constexpr bool F32 = Path<InT>::kF32;
+  constexpr int NM = DK / 16;
+  constexpr int LDK = DK + 4;  // padded LDS row (conflict-free transposed reads)
+  __shared__ float s_beta[16];
+  __shared__ float s_kt[16 * LDK];
+  __shared__ float s_kb[16 * LDK];
+  __shared__ float s_A[16][17];
+  __shared__ float s_M[16][17];
+  __shared__ float s_T[16][17];
+
+  const int l = threadIdx.x, c16 = l & 15, gq = l >> 4;
+  const int64_t wg = blockIdx.x;  // ((b * NC) + n) * H + h
+  const int64_t h = wg % H;
+  const int64_t bn = wg / H;
+  const int64_t n = bn % NC;
+  const int64_t b = bn / NC;
+  const int64_t t = n * 16 + c16;
+  const bool valid = t < T;
+  const size_t tok = static_cast<size_t>((b * T + (valid ? t : 0)) * H + h);
+
+  // ---- load this lane's token: 4*NM channels of q, k, g ----
+  float xq[NM][4], xk[NM][4], xg[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const size_t off = tok * DK + 16 * m + 4 * gq;
+    if (valid) {
+      load_in4(q, off, xq[m]);
+      load_in4(k, off, xk[m]);
+      load_in4(g, off, xg[m]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xq[m][i] = xk[m][i] = xg[m][i] = 0.f;
+    }
+  }
+  if (gq == 0) s_beta[c16] = valid ? load_in(beta, tok) : 0.f;
+
+  // ---- per-channel cumulative log-decay over the chunk (base 2) ----
+  float E[NM][4], Eh[NM][4], Eb[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = clamp_decay(xg[m][i]) * kLog2e;
+      const float G = row_inclusive_prefix_sum(x);    // log2 e^Gamma_r
+      const float Gb = row_exclusive_suffix_sum(x);   // log2 e^(gamma - Gamma_r)
+      E[m][i] = exp2f(G);
+      Eh[m][i] = exp2f(-G);
+      Eb[m][i] = exp2f(Gb);
+    }
+  }
+
+  // ---- scaled operands ----
+  float qt[NM][4], kt[NM][4], kh[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qt[m][i] = E[m][i] * xq[m][i];
+      kt[m][i] = E[m][i] * xk[m][i];
+      kh[m][i] = Eh[m][i] * xk[m][i];
+      s_kt[c16 * LDK + 16 * m + 4 * gq + i] = kt[m][i];
+      s_kb[c16 * LDK + 16 * m + 4 * gq + i] = Eb[m][i] * xk[m][i];
+    }
+  }
+
+  // ---- chunk Gram tiles: Araw = Kt Kh^T, Mraw = Qt Kh^T (16 x 16) ----
+  f32x4 Araw = zero4(), Mraw = zero4();
+  if constexpr (F32) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Araw = mma_16x16x4_f32(kt[m][i], kh[m][i], Araw);
+        Mraw = mma_16x16x4_f32(qt[m][i], kh[m][i], Mraw);
+      }
+  } else {
+    // bf16 operands carry the e^{+-Gamma} range; each is split into a bf16
+    // high part and a bf16 remainder (hi*hi + hi*lo + lo*hi) for accuracy.
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      bf16x8 kt_hi, kt_lo, kh_hi, kh_lo, qt_hi, qt_lo;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = 2 * p + (j >> 2), i = j & 3;
+        kt_hi[j] = static_cast<__bf16>(kt[m][i]);
+        kt_lo[j] = static_cast<__bf16>(kt[m][i] - static_cast<float>(kt_hi[j]));
+        kh_hi[j] = static_cast<__bf16>(kh[m][i]);
+        kh_lo[j] = static_cast<__bf16>(kh[m][i] - static_cast<float>(kh_hi[j]));
+        qt_hi[j] = static_cast<__bf16>(qt[m][i]);
+        qt_lo[j] = static_cast<__bf16>(qt[m][i] - static_cast<float>(qt_hi[j]));
+      }
+      Araw = mma_16x16x32_bf16(kt_hi, kh_hi, Araw);
+      Araw = mma_16x16x32_bf16(kt_hi, kh_lo, Araw);
+      Araw = mma_16x16x32_bf16(kt_lo, kh_hi, Araw);
+      Mraw = mma_16x16x32_bf16(qt_hi, kh_hi, Mraw);
+      Mraw = mma_16x16x32_bf16(qt_hi, kh_lo, Mraw);
+      Mraw = mma_16x16x32_bf16(qt_lo, kh_hi, Mraw);
+    }
+  }
+  __syncthreads();  // s_beta, s_kt, s_kb visible
+
+  // ---- masks: A strictly lower with row scale beta_r, M lower incl. diag ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * gq + i, s = c16;
+    s_A[r][s] = (s < r) ? s_beta[r] * Araw[i] : 0.f;
+    s_M[r][s] = (s <= r) ? Mraw[i] : 0.f;
+  }
+  __syncthreads();
+
+  // ---- Tm = (I + A)^-1, column c16 per lane, by forward substitution ----
+  // Tm[r][j] = delta_rj - sum_{s<r} A[r][s] Tm[s][j] (A strictly lower).
+  {
+    float tc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == c16) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= s_A[r][s] * tc[s];
+      tc[r] = acc;
+    }
+    if (gq == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_T[r][c16] = tc[r];
+    }
+  }
+  __syncthreads();
+
+  float tb[4], mf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = 4 * gq + i;
+    tb[i] = s_T[c16][s] * s_beta[s];
+    mf[i] = s_M[c16][s];
+  }
+
+  // ---- W^T tiles = Kt^T (diag(beta) Tm^T): lane gets W[c16][16m+4gq+i] ----
+  float w[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = s_kt[(4 * gq + i) * LDK + 16 * m + c16];
+    f32x4 acc = zero4();
+    if constexpr (F32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = mma_16x16x4_f32(a[i], tb[i], acc);
+    } else {
+      f16x4 av, bv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = static_cast<_Float16>(a[i]);
+        bv[i] = static_cast<_Float16>(tb[i]);
+      }
+      acc = mma_16x16x16_f16(av, bv, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[m][i] = acc[i];
+  }
+
+  // ---- write the record ----
+  uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NC + n) * L.bytes;
+  using Op = typename Path<InT>::Op;
+  if constexpr (F32) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const size_t off = static_cast<size_t>(m * 64 + l) * 16;
+      *reinterpret_cast<float4*>(rec + L.w + off) = make_float4(-w[m][0], -w[m][1], -w[m][2], -w[m][3]);
+      *reinterpret_cast<float4*>(rec + L.q + off) = make_float4(qt[m][0], qt[m][1], qt[m][2], qt[m][3]);
+      float kb4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kb4[i] = s_kb[(4 * gq + i) * LDK + 16 * m + c16];
+      *reinterpret_cast<float4*>(rec + L.kbar + off) = make_float4(kb4[0], kb4[1], kb4[2], kb4[3]);
+    }
+    *reinterpret_cast<float4*>(rec + L.m + l * 16) = make_float4(mf[0], mf[1], mf[2], mf[3]);
+    *reinterpret_cast<float4*>(rec + L.tb + l * 16) = make_float4(tb[0], tb[1], tb[2], tb[3]);
+  } else {
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      f16x8 wv, qv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = 2 * p + (j >> 2), i = j & 3;
+        wv[j] = static_cast<Op>(-w[m][i]);
+        qv[j] = static_cast<Op>(qt[m][i]);
+      }
+      const size_t off = static_cast<size_t>(p * 64 + l) * 16;
+      *reinterpret_cast<f16x8*>(rec + L.w + off) = wv;
+      *reinterpret_cast<f16x8*>(rec + L.q + off) = qv;
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      f16x4 kv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[i] = static_cast<Op>(s_kb[(4 * gq + i) * LDK + 16 * m + c16]);
+      *reinterpret_cast<f16x4*>(rec + L.kbar + static_cast<size_t>(m * 64 + l) * 8) = kv;
+    }
+    f16x4 mh, ml, tv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mh[i] = static_cast<Op>(mf[i]);
+      ml[i] = static_cast<Op>(mf[i] - static_cast<float>(mh[i]));
+      tv[i] = static_cast<Op>(tb[i]);
+    }
+    *reinterpret_cast<f16x4*>(rec + L.m + l * 8) = mh;
+    *reinterpret_cast<f16x4*>(rec + L.m + 512 + l * 8) = ml;
+    *reinterpret_cast<f16x4*>(rec + L.tb + l * 8) = tv;
+  }
+  if (c16 == 15) {  // e^gamma for this lane's channels
+    float* eg = reinterpret_cast<float*>(rec + L.eg) + gq * (DK / 4);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      *reinterpret_cast<float4*>(eg + 4 * m) = make_float4(E[m][0], E[m][1], E[m][2], E[m][3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sequential state pass.
+// ---------------------------------------------------------------------------
+
+template <typename InT, int DK>
+struct ChunkFrags {
+  static constexpr bool F32 = Path<InT>::kF32;
+  static constexpr int NM = DK / 16;
+  // W and Q: fp16 -> NM/2 x 8 halves; fp32 -> NM x 4 floats (same values)
+  typename std::conditional<F32, f32x4, f16x8>::type w[F32 ? NM : NM / 2];
+  typename std::conditional<F32, f32x4, f16x8>::type q[F32 ? NM : NM / 2];
+  typename std::conditional<F32, f32x4, f16x4>::type kb[NM];
+  typename std::conditional<F32, f32x4, f16x4>::type mh, ml, tb;
+  f32x4 eg[NM];
+  float vv[4];
+
+  __device__ __forceinline__ void load(const uint8_t* rec, const RecordLayout& L, int l, int gq,
+                                       const InT* v, size_t vbase, int64_t tok0, int64_t T,
+                                       int64_t H, int64_t DV) {
+    if constexpr (F32) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const size_t off = static_cast<size_t>(m * 64 + l) * 16;
+        w[m] = *reinterpret_cast<const f32x4*>(rec + L.w + off);
+        q[m] = *reinterpret_cast<const f32x4*>(rec + L.q + off);
+        kb[m] = *reinterpret_cast<const f32x4*>(rec + L.kbar + off);
+      }
+      mh = *reinterpret_cast<const f32x4*>(rec + L.m + l * 16);
+      tb = *reinterpret_cast<const f32x4*>(rec + L.tb + l * 16);
+    } else {
+#pragma unroll
+      for (int p = 0; p < NM / 2; ++p) {
+        const size_t off = static_cast<size_t>(p * 64 + l) * 16;
+        w[p] = *reinterpret_cast<const f16x8*>(rec + L.w + off);
+        q[p] = *reinterpret_cast<const f16x8*>(rec + L.q + off);
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        kb[m] = *reinterpret_cast<const f16x4*>(rec + L.kbar + static_cast<size_t>(m * 64 + l) * 8);
+      mh = *reinterpret_cast<const f16x4*>(rec + L.m + l * 8);
+      ml = *reinterpret_cast<const f16x4*>(rec + L.m + 512 + l * 8);
+      tb = *reinterpret_cast<const f16x4*>(rec + L.tb + l * 8);
+    }
+    const f32x4* egp = reinterpret_cast<const f32x4*>(rec + L.eg) + gq * NM;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) eg[m] = egp[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = tok0 + 4 * gq + i;
+      vv[i] = (t < T) ? load_in(v, vbase + static_cast<size_t>(t * H) * DV) : 0.f;
+    }
+  }
+};
+
+template <typename InT, typename OutT, int DK>
+__global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
+                                                     const uint8_t* __restrict__ ws,
+                                                     const float* S0, OutT* __restrict__ o,
+                                                     float* ST, int64_t T, int64_t H,
+                                                     int64_t DV, int64_t NC, int64_t nslices,
+                                                     int64_t nheads, RecordLayout L) {
+  constexpr bool F32 = Path<InT>::kF32;
+  constexpr int NM = DK / 16;
+  const int l = threadIdx.x, c16 = l & 15, gq = l >> 4;
+
+  // XCD-aware numbering: workgroups are dealt round-robin to the 8 XCDs, so
+  // all slices of one head get ids congruent mod 8 and share an XCD's L2
+  // for the head's workspace records.
+  const int64_t wgid = blockIdx.x;
+  const int64_t xcd = wgid & 7, kk = wgid >> 3;
+  const int64_t head = xcd + 8 * (kk / nslices);
+  const int64_t slice = kk % nslices;
+  if (head >= nheads) return;
+  const int64_t b = head / H, h = head % H;
+  const int64_t col = slice * 16 + c16;
+
+  // state slice: S[m][i] = S[16m + 4gq + i][col]
+  f32x4 S[NM];
+  const size_t sbase = static_cast<size_t>(head) * DK * DV + col;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+
+  const uint8_t* rec0 = ws + static_cast<size_t>(head) * NC * L.bytes;
+  const size_t vbase = static_cast<size_t>(b * T * H + h) * DV + col;
+
+  ChunkFrags<InT, DK> cur, nxt;
+  cur.load(rec0, L, l, gq, v, vbase, 0, T, H, DV);
+  for (int64_t n = 0; n < NC; ++n) {
+    if (n + 1 < NC) nxt.load(rec0 + static_cast<size_t>(n + 1) * L.bytes, L, l, gq, v, vbase,
+                             (n + 1) * 16, T, H, DV);
+    f32x4 U, O;
+    if constexpr (F32) {
+      // Ut = Tb V
+      U = zero4();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U = mma_16x16x4_f32(cur.tb[i], cur.vv[i], U);
+      // U = Ut - W S ; O = Qt S
+      O = zero4();
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          U = mma_16x16x4_f32(cur.w[m][i], S[m][i], U);
+          O = mma_16x16x4_f32(cur.q[m][i], S[m][i], O);
+        }
+      // O += M U
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O = mma_16x16x4_f32(cur.mh[i], U[i], O);
+      // S = Diag(e^gamma) S + Kb^T U
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        S[m] = S[m] * cur.eg[m];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[m] = mma_16x16x4_f32(cur.kb[m][i], U[i], S[m]);
+      }
+    } else {
+      // Every accumulation chain below uses one MFMA shape (16x16x32). Two
+      // shapes chained through an accumulator need wait states on gfx950
+      // that the compiler does not insert; the 16-deep token contractions
+      // are therefore issued as 16x16x32 with the upper 16 slots zero (or,
+      // for M U, holding the low-order part of M against a second copy of U).
+      f16x8 tbz, vz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tbz[i] = cur.tb[i];
+        tbz[i + 4] = static_cast<_Float16>(0.f);
+        vz[i] = static_cast<_Float16>(cur.vv[i]);
+        vz[i + 4] = static_cast<_Float16>(0.f);
+      }
+      U = mma_16x16x32_f16(tbz, vz, zero4());          // Ut = Tb V
+      f16x8 sh[NM / 2];
+#pragma unroll
+      for (int p = 0; p < NM / 2; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
+      O = zero4();
+#pragma unroll
+      for (int p = 0; p < NM / 2; ++p) {
+        U = mma_16x16x32_f16(cur.w[p], sh[p], U);      // U = Ut - W S
+        O = mma_16x16x32_f16(cur.q[p], sh[p], O);      // O = Qt S
+      }
+      f16x8 uu, uz, mhl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 x = static_cast<_Float16>(U[i]);
+        uu[i] = x;
+        uu[i + 4] = x;
+        uz[i] = x;
+        uz[i + 4] = static_cast<_Float16>(0.f);
+        mhl[i] = cur.mh[i];
+        mhl[i + 4] = cur.ml[i];
+      }
+      O = mma_16x16x32_f16(mhl, uu, O);                // O += (Mhi + Mlo) U
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {                   // S = Diag(e^gamma) S + Kb^T U
+        f16x8 kz;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kz[i] = cur.kb[m][i];
+          kz[i + 4] = static_cast<_Float16>(0.f);
+        }
+        S[m] = mma_16x16x32_f16(kz, uz, S[m] * cur.eg[m]);
+      }
+    }
+    // o rows 4gq + i of this chunk, column col
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = n * 16 + 4 * gq + i;
+      if (t < T) store_out(o, vbase + static_cast<size_t>(t * H) * DV, O[i]);
+    }
+    if (n + 1 < NC) cur = nxt;
+  }
+  if (ST) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ST[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] = S[m][i];
+  }
+}
+
+// T = 0: the final state is the initial one (or zeros).
+__global__ void kda_copy_state(const float* S0, float* ST, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) ST[i] = S0 ? S0[i] : 0.f;
+}
+
+template <typename InT, typename OutT, int DK>
+hipError_t launch_typed(const ChunkFwdArgs& a, hipStream_t stream) {
+  constexpr bool F32 = Path<InT>::kF32;
+  const RecordLayout L = record_layout(DK, F32);
+  const int64_t NC = (a.T + 15) / 16;
+  const int64_t nheads = a.B * a.H;
+  const int64_t prep_blocks = a.B * NC * a.H;
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  hipLaunchKernelGGL((kda_chunk_prep<InT, DK>), dim3(static_cast<uint32_t>(prep_blocks)), dim3(64),
+                     0, stream, static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
+                     static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta), ws, a.T, a.H,
+                     NC, L);
+  const int64_t nslices = a.dv / 16;
+  const int64_t groups = (nheads + 7) / 8;
+  const int64_t pass_blocks = 8 * nslices * groups;
+  hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(pass_blocks)),
+                     dim3(64), 0, stream, static_cast<const InT*>(a.v), ws, a.S0,
+                     static_cast<OutT*>(a.o), a.S_T, a.T, a.H, a.dv, NC, nslices, nheads, L);
+  return hipGetLastError();
+}
+
+template <typename InT, typename OutT>
+hipError_t launch_dk(const ChunkFwdArgs& a, hipStream_t s) {
+  return a.dk == 64 ? launch_typed<InT, OutT, 64>(a, s) : launch_typed<InT, OutT, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream) {
+  const int64_t nheads = a.B * a.H;
+  if (nheads == 0) return hipSuccess;
+  if (a.T == 0) {
+    if (a.S_T && a.S_T != a.S0) {
+      const int64_t n = nheads * a.dk * a.dv;
+      hipLaunchKernelGGL(kda_copy_state, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                         stream, a.S0, a.S_T, n);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+  const bool in32 = a.in_dtype == 0, out32 = a.out_dtype == 0;
+  if (in32) return out32 ? launch_dk<float, float>(a, stream) : launch_dk<float, uint16_t>(a, stream);
+  return out32 ? launch_dk<uint16_t, float>(a, stream) : launch_dk<uint16_t, uint16_t>(a, stream);
+}
+
+}  // namespace kda

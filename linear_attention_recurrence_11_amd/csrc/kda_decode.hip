@@ -1,0 +1,130 @@
+// One KDA decode step on gfx950: a single token for each of N requests.
+//
+// Per (request, head) with fp32 state S (dk x dv), in place:
+//   S' = Diag(e^g) S;  r = S'^T k;  p = S'^T q;  u = beta (v - r);
+//   S  = S' + k u^T;   o = S^T q = p + (q . k) u
+// The step is the T = 1 case of the recurrence: the fixed-size state is read
+// and overwritten for every token ("177: Kimi K3 in Detail", sections 10 and
+// 17: decoding re-reads the whole recurrent state per token). Memory-bound:
+// each state is streamed from HBM once and written back once, held in
+// registers in between.
+//
+// Workgroup of 256 threads per (request, head). Thread t owns the float4
+// column group cg = t % (dv/4) of rows rg + RG*j (RG = 256/(dv/4)), so one
+// load instruction of a wavefront covers whole 512-byte rows (coalesced).
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+template <typename InT, typename OutT, int DK, int DV>
+__global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__ q,
+                                                         const InT* __restrict__ k,
+                                                         const InT* __restrict__ v,
+                                                         const InT* __restrict__ g,
+                                                         const InT* __restrict__ beta,
+                                                         float* __restrict__ S,
+                                                         OutT* __restrict__ o) {
+  constexpr int CPR = DV / 4;     // threads per row
+  constexpr int RG = 256 / CPR;   // row groups
+  constexpr int RPT = DK / RG;    // rows per thread
+  static_assert(RPT >= 1 && DK % RG == 0, "shape");
+  __shared__ float s_q[DK], s_k[DK], s_e[DK];
+  __shared__ float s_red[2][RG][DV + 4];
+  __shared__ float s_u[DV];
+  __shared__ float s_qk;
+
+  const int t = threadIdx.x;
+  const int cg = t % CPR, rg = t / CPR;
+  const size_t unit = blockIdx.x;  // n * H + h
+  float* Su = S + unit * DK * DV;
+
+  // stream the state in first (independent of everything else)
+  float4 s[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    s[j] = *reinterpret_cast<const float4*>(Su + static_cast<size_t>(rg + RG * j) * DV + 4 * cg);
+
+  for (int i = t; i < DK; i += 256) {
+    s_q[i] = load_in(q, unit * DK + i);
+    s_k[i] = load_in(k, unit * DK + i);
+    s_e[i] = expf(clamp_decay(load_in(g, unit * DK + i)));
+  }
+  __syncthreads();
+  if (t < 64) {  // q . k by one wavefront
+    float acc = 0.f;
+    for (int i = t; i < DK; i += 64) acc += s_q[i] * s_k[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (t == 0) s_qk = acc;
+  }
+
+  // S' = Diag(e) S ; partial r and p over this thread's rows
+  float r4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int row = rg + RG * j;
+    const float e = s_e[row], kr = s_k[row], qr = s_q[row];
+    s[j].x *= e; s[j].y *= e; s[j].z *= e; s[j].w *= e;
+    r4[0] += kr * s[j].x; r4[1] += kr * s[j].y; r4[2] += kr * s[j].z; r4[3] += kr * s[j].w;
+    p4[0] += qr * s[j].x; p4[1] += qr * s[j].y; p4[2] += qr * s[j].z; p4[3] += qr * s[j].w;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s_red[0][rg][4 * cg + c] = r4[c];
+    s_red[1][rg][4 * cg + c] = p4[c];
+  }
+  __syncthreads();
+  if (t < DV) {
+    float r = 0.f, p = 0.f;
+#pragma unroll
+    for (int x = 0; x < RG; ++x) {
+      r += s_red[0][x][t];
+      p += s_red[1][x][t];
+    }
+    const float u = load_in(beta, unit) * (load_in(v, unit * DV + t) - r);
+    s_u[t] = u;
+    store_out(o, unit * DV + t, p + s_qk * u);
+  }
+  __syncthreads();
+
+  // S = S' + k u^T, written back
+  const float u0 = s_u[4 * cg], u1 = s_u[4 * cg + 1], u2 = s_u[4 * cg + 2], u3 = s_u[4 * cg + 3];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int row = rg + RG * j;
+    const float kr = s_k[row];
+    float4 x = s[j];
+    x.x += kr * u0; x.y += kr * u1; x.z += kr * u2; x.w += kr * u3;
+    *reinterpret_cast<float4*>(Su + static_cast<size_t>(row) * DV + 4 * cg) = x;
+  }
+}
+
+template <typename InT, typename OutT, int DK, int DV>
+hipError_t launch4(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t units = a.N * a.H;
+  hipLaunchKernelGGL((kda_decode_kernel<InT, OutT, DK, DV>), dim3(static_cast<uint32_t>(units)),
+                     dim3(256), 0, stream, static_cast<const InT*>(a.q),
+                     static_cast<const InT*>(a.k), static_cast<const InT*>(a.v),
+                     static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta), a.S,
+                     static_cast<OutT*>(a.o));
+  return hipGetLastError();
+}
+
+template <typename InT, typename OutT>
+hipError_t launch2(const DecodeArgs& a, hipStream_t s) {
+  if (a.dk == 64) return a.dv == 64 ? launch4<InT, OutT, 64, 64>(a, s) : launch4<InT, OutT, 64, 128>(a, s);
+  return a.dv == 64 ? launch4<InT, OutT, 128, 64>(a, s) : launch4<InT, OutT, 128, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream) {
+  if (a.N * a.H == 0) return hipSuccess;
+  const bool in32 = a.in_dtype == 0, out32 = a.out_dtype == 0;
+  if (in32) return out32 ? launch2<float, float>(a, stream) : launch2<float, uint16_t>(a, stream);
+  return out32 ? launch2<uint16_t, float>(a, stream) : launch2<uint16_t, uint16_t>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,118 @@
+// Device-side building blocks for the KDA kernels on gfx950 (CDNA4):
+// 64-lane wavefront matrix-core (MFMA) wrappers, DPP row scans, and
+// element conversions. Everything here is wave-level and header-only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kChunk = 16;  // tokens per chunk (one MFMA tile edge)
+
+// ---- element conversions -------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Input element loads: T is float (fp32 inputs) or uint16_t (bf16 bits).
+template <typename T> __device__ __forceinline__ float load_in(const T* p, size_t i);
+template <> __device__ __forceinline__ float load_in<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+// Four consecutive input elements starting at p[i] (i a multiple of 4).
+template <typename T> __device__ __forceinline__ void load_in4(const T* p, size_t i, float out[4]);
+template <> __device__ __forceinline__ void load_in4<float>(const float* p, size_t i, float out[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p + i);
+  out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+}
+template <> __device__ __forceinline__ void load_in4<uint16_t>(const uint16_t* p, size_t i, float out[4]) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p + i);
+  out[0] = __uint_as_float(x.x << 16);
+  out[1] = __uint_as_float(x.x & 0xffff0000u);
+  out[2] = __uint_as_float(x.y << 16);
+  out[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
+template <typename T> __device__ __forceinline__ void store_out(T* p, size_t i, float x);
+template <> __device__ __forceinline__ void store_out<float>(float* p, size_t i, float x) { p[i] = x; }
+template <> __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, size_t i, float x) {
+  p[i] = f32_to_bf16_bits(x);
+}
+
+// Log-decay floor: clamp to [-5, 0] with comparisons, so NaN stays NaN.
+__device__ __forceinline__ float clamp_decay(float x) {
+  return x < -5.0f ? -5.0f : (x > 0.0f ? 0.0f : x);
+}
+
+// ---- DPP row scans (a row is 16 consecutive lanes) -----------------------
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float x) {
+  // Lanes whose source falls outside the row receive 0.0f.
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+
+// Inclusive prefix sum over the 16 lanes of each row (lane r gets sum of
+// lanes 0..r of its row): Hillis-Steele with row_shr:1,2,4,8.
+__device__ __forceinline__ float row_inclusive_prefix_sum(float x) {
+  x += dpp_move<0x111>(x);
+  x += dpp_move<0x112>(x);
+  x += dpp_move<0x114>(x);
+  x += dpp_move<0x118>(x);
+  return x;
+}
+
+// Exclusive suffix sum over the row (lane r gets sum of lanes r+1..15).
+__device__ __forceinline__ float row_exclusive_suffix_sum(float x) {
+  float y = dpp_move<0x101>(x);  // row_shl:1
+  y += dpp_move<0x101>(y);
+  y += dpp_move<0x102>(y);
+  y += dpp_move<0x104>(y);
+  y += dpp_move<0x108>(y);
+  return y;
+}
+
+// ---- MFMA wrappers (16x16 output tiles, fp32 accumulate) -----------------
+// Output layout for every 16x16 tile: lane l holds rows 4*(l/16)+i, i=0..3,
+// of column l%16. Operand layouts (checked on gfx950): 16x16x16 f16 lane l
+// holds A[l%16][4*(l/16)+i] and B[4*(l/16)+i][l%16]; 16x16x32 f16/bf16 holds
+// A[l%16][8*(l/16)+j] and B[8*(l/16)+j][l%16]; 16x16x4 f32 holds A[l%16][l/16]
+// and B[l/16][l%16].
+// On gfx950 an accumulator written by one MFMA shape and read as the
+// accumulator input of a different shape (16x16x16 <-> 16x16x32) needs about
+// six wait states that the compiler does not insert (the later MFMA then sees
+// stale elements). Chains of one shape are interlocked by the hardware, so
+// every accumulation chain in these kernels uses a single shape.
+
+__device__ __forceinline__ f32x4 mma_16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_16x16x16_f16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_16x16x4_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace kda

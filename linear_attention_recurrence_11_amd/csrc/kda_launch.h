@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI host layer (kda_api.cpp) and the HIP
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int64_t kChunkTokens = 16;
+
+// Per-(batch, head, chunk) workspace record written by the chunk-prep kernel
+// and read by the state-pass kernel. Offsets in bytes; total is a multiple of
+// 256. `es` is the element size of the matrix-core operands it holds (2 for
+// the fp16 operands of the bf16-input path, 4 for the fp32 path).
+struct RecordLayout {
+  int64_t es, w, q, kbar, m, tb, eg, bytes;
+};
+
+inline RecordLayout record_layout(int64_t dk, bool f32_path) {
+  RecordLayout L;
+  L.es = f32_path ? 4 : 2;
+  const int64_t tile = dk * kChunkTokens * L.es;     // 16 tokens x dk operand
+  L.w = 0;
+  L.q = tile;
+  L.kbar = 2 * tile;
+  L.m = 3 * tile;
+  const int64_t msz = 256 * L.es * (f32_path ? 1 : 2);  // fp16: hi and lo parts
+  L.tb = L.m + msz;
+  L.eg = L.tb + 256 * L.es;
+  const int64_t end = L.eg + dk * 4;
+  L.bytes = (end + 255) / 256 * 256;
+  return L;
+}
+
+struct ChunkFwdArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* S0;
+  void* o;
+  float* S_T;
+  int64_t B, T, H, dk, dv;
+  int in_dtype, out_dtype;  // kda_dtype values
+  void* workspace;
+};
+
+struct DecodeArgs {
+  const void *q, *k, *v, *g, *beta;
+  float* S;
+  void* o;
+  int64_t N, H, dk, dv;
+  int in_dtype, out_dtype;
+};
+
+// Launch the chunkwise forward (prep kernel then state pass) on `stream`.
+hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream);
+
+// Launch one decode step on `stream`.
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kda

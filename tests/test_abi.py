@@ -1,0 +1,169 @@
+"""The C-ABI library loads on the CPU and exports every symbol include/kda.h
+declares; host-side argument checks behave as documented (no GPU used: only
+calls that are rejected before any HIP call, and the pure host functions)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_11_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+OK, NULL, SHAPE, UNSUP, ALIAS, WS, HIP, ALIGN = range(8)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from linear_attention_recurrence_11_amd import build
+        build.build()
+    return binding._load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "libkda.so does not export %s" % n
+
+
+def test_version_and_status_strings(lib):
+    assert binding.kda_abi_version() == 1
+    for s in range(8):
+        assert binding.kda_status_str(s) and binding.kda_status_str(s) != "unknown status"
+    assert binding.kda_status_str(99) == "unknown status"
+
+
+def test_workspace_size(lib):
+    # 16-token chunks; one record per (b, h, chunk): 14336 B (bf16 in, dk 128),
+    # 27136 B (fp32 in, dk 128)
+    assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == 32 * 4096 * 14336
+    assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == 64 * 256 * 14336
+    assert binding.kda_chunk_fwd_workspace_size(1, 256, 2, 64, 64, F32) == 2 * 16 * 14592
+    assert binding.kda_chunk_fwd_workspace_size(1, 17, 1, 128, 128, F32) == 2 * 27136
+    assert binding.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, F32) == 0
+    assert binding.kda_chunk_fwd_workspace_size(1, 16, 1, 96, 128, F32) == 0
+    assert binding.kda_chunk_fwd_workspace_size(1, 16, 1, 128, 24, F32) == 0
+
+
+BASE = 1 << 40   # fake, never dereferenced, 16-byte aligned addresses
+
+
+def fake_chunk(B=1, T=32, H=2, dk=64, dv=64, ind=F32, outd=F32, s0=True, st=True, ws=True):
+    es = 4 if ind == F32 else 2
+    n = B * T * H
+    off = [BASE]
+
+    def alloc(nbytes):
+        p = off[0]
+        off[0] += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+    p = dict(q=alloc(n * dk * es), k=alloc(n * dk * es), v=alloc(n * dv * es),
+             g=alloc(n * dk * es), beta=alloc(n * es),
+             S0=alloc(B * H * dk * dv * 4) if s0 else None,
+             o=alloc(n * dv * (4 if outd == F32 else 2)),
+             S_T=alloc(B * H * dk * dv * 4) if st else None)
+    need = binding.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, ind)
+    p["ws"] = alloc(need) if ws else None
+    p["ws_bytes"] = need
+    return p, (B, T, H, dk, dv, ind, outd)
+
+
+def check(lib, p, sizes, **over):
+    p = dict(p)
+    p.update(over)
+    B, T, H, dk, dv, ind, outd = sizes
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return lib.kda_chunk_fwd_check(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]), vp(p["beta"]),
+                                   vp(p["S0"]), vp(p["o"]), vp(p["S_T"]), B, T, H, dk, dv, ind,
+                                   outd, vp(p["ws"]), p["ws_bytes"])
+
+
+def test_chunk_check_accepts_valid(lib):
+    for kw in (dict(), dict(ind=BF16), dict(ind=BF16, outd=BF16, dk=128, dv=128),
+               dict(dv=16), dict(dv=512), dict(T=1), dict(T=17), dict(s0=False, st=False)):
+        p, sz = fake_chunk(**kw)
+        assert check(lib, p, sz) == OK, kw
+
+
+def test_chunk_check_rejects(lib):
+    p, sz = fake_chunk()
+    assert check(lib, p, sz, q=None) == NULL
+    assert check(lib, p, sz, o=None) == NULL
+    assert check(lib, p, sz, ws=None) == WS
+    assert check(lib, p, sz, ws_bytes=p["ws_bytes"] - 1) == WS
+    assert check(lib, p, sz, q=p["q"] + 8) == ALIGN         # fp32 q: 4-element vectors
+    assert check(lib, p, sz, ws=p["ws"] + 8) == ALIGN
+    assert check(lib, p, sz, beta=p["beta"] + 2) == ALIGN
+    assert check(lib, p, sz, beta=p["beta"] + 4) == OK      # element-aligned is enough
+    assert check(lib, p, sz, o=p["o"] + 4) == OK
+    assert check(lib, p, sz, o=p["q"]) == ALIAS            # o over q
+    assert check(lib, p, sz, o=p["S0"]) == ALIAS           # o over S0
+    assert check(lib, p, sz, S_T=p["S0"] + 64) == ALIAS    # partial state overlap
+    assert check(lib, p, sz, S_T=p["S0"]) == OK            # exact alias: in place
+    assert check(lib, p, sz, ws=p["v"]) == ALIAS           # workspace over v
+    B, T, H, dk, dv, ind, outd = sz
+    assert check(lib, p, (B, -1, H, dk, dv, ind, outd)) == SHAPE
+    assert check(lib, p, (B, T, H, 96, dv, ind, outd)) == UNSUP
+    assert check(lib, p, (B, T, H, dk, 24, ind, outd)) == UNSUP
+    assert check(lib, p, (B, T, H, dk, 528, ind, outd)) == UNSUP
+    assert check(lib, p, (B, T, H, dk, dv, 7, outd)) == UNSUP
+    assert check(lib, p, (B, T, H, dk, dv, ind, 5)) == UNSUP
+
+
+def test_chunk_empty_needs_nothing(lib):
+    p, sz = fake_chunk()
+    B, T, H, dk, dv, ind, outd = sz
+    nulls = dict(q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, ws_bytes=0)
+    assert check(lib, p, (B, 0, H, dk, dv, ind, outd), **nulls) == OK
+    assert check(lib, p, (0, T, H, dk, dv, ind, outd), **nulls) == OK
+
+
+def test_chunk_fwd_rejects_before_any_launch(lib):
+    """kda_chunk_fwd returns the check's error without touching the GPU."""
+    p, sz = fake_chunk()
+    B, T, H, dk, dv, ind, outd = sz
+    vp = ctypes.c_void_p
+    st = lib.kda_chunk_fwd(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]), vp(p["beta"]),
+                           vp(p["S0"]), vp(p["q"]), vp(p["S_T"]), B, T, H, dk, dv, ind, outd,
+                           vp(p["ws"]), p["ws_bytes"], None)
+    assert st == ALIAS
+    st = lib.kda_chunk_fwd(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]), vp(p["beta"]),
+                           vp(p["S0"]), vp(p["o"]), vp(p["S_T"]), B, T, H, 80, dv, ind, outd,
+                           vp(p["ws"]), p["ws_bytes"], None)
+    assert st == UNSUP
+    # empty work returns OK without a launch
+    st = lib.kda_chunk_fwd(None, None, None, None, None, None, None, None, 0, 5, 3, 64, 64, 0, 0,
+                           None, 0, None)
+    assert st == OK
+
+
+def test_decode_check(lib):
+    vp = ctypes.c_void_p
+    N, H, dk, dv = 4, 2, 128, 128
+    a = [BASE + i * (1 << 24) for i in range(7)]   # q k v g beta S o
+    call = lambda ptrs, N=N, H=H, dk=dk, dv=dv, ind=BF16, outd=F32: lib.kda_decode_step_check(
+        *[vp(x) if x is not None else None for x in ptrs], N, H, dk, dv, ind, outd)
+    assert call(a) == OK
+    assert call(a, dk=64, dv=64) == OK
+    assert call(a, dv=96) == UNSUP
+    assert call(a[:6] + [a[5]]) == ALIAS        # o over S
+    assert call(a[:5] + [a[0]] + [a[6]]) == ALIAS   # S over q
+    assert call([None] + a[1:]) == NULL
+    assert call(a[:6] + [a[6] + 2]) == ALIGN                # fp32 o
+    assert call(a[:6] + [a[6] + 4]) == OK
+    assert call(a[:5] + [a[5] + 8] + [a[6]]) == ALIGN       # state: 16 bytes
+    assert call([a[0] + 2] + a[1:]) == OK                    # bf16 q: element-aligned
+    assert call(a, N=-1) == SHAPE
+    assert call([None] * 7, N=0) == OK
+    st = lib.kda_decode_step(*[vp(x) for x in a[:6]], vp(a[5]), N, H, dk, dv, BF16, F32, None)
+    assert st == ALIAS

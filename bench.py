@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""KDA on one MI355X: prefill tokens/s at H=32, d=128, T=64K and decode state
+GB/s, each against its roofline, with the fp64 oracle timed on the host.
+
+One step = the whole hot path over one batch of synthetic input:
+  prefill  kda_chunk_prep + kda_chunk_state_pass (= kda_chunk_fwd) over
+           B=1, T=65536, H=32, dk=dv=128, bf16 inputs, fp32 state and output
+  decode   64 kda_decode_step launches over N=256 requests x H=32 heads with
+           resident fp32 states (128x128), bf16 per-token inputs
+Inputs are generated on the GPU before timing (seeded, synthetic). Every
+kernel launch is bracketed by HIP events on the stream it runs on.
+
+Prints one JSON line. `value` is prefill tokens/s (B*T / prefill time).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=32,d=128,T=64K) + decode state GB/s, % of roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def prefill_units(B, T, H, dk, dv, C=16):
+    """Algorithmic work per token-head of the prefill path (bf16 in, fp32 o):
+    flops 6 dk dv + 4C dk + 2C dv + C(dk+dv); bytes q,k,g,v (bf16) + beta + o."""
+    flops = 6 * dk * dv + 4 * C * dk + 2 * C * dv + C * (dk + dv)
+    bytes_ = 2 * (3 * dk + dv) + 2 + 4 * dv
+    return flops, bytes_
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel):
+    """HBM traffic per dispatch measured with rocprofv3 counters, if it was
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_sha256") != source_sha(ent.get("sources", [])):
+        return None
+    return ent.get("bytes_per_dispatch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
+                    help="tokens (all 32 heads) of the prefill workload the oracle runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested). Run with --gpus 1." % args.gpus, file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrence_11_amd import binding, configs, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pf = configs.PREFILL_64K
+    dc = configs.DECODE
+    B, T, H, dk, dv = pf.B, pf.T, pf.H, pf.dk, pf.dv
+    print("[bench] generating %s and %s" % (pf.name, dc.name), file=sys.stderr, flush=True)
+    ins = inputs.make_workload(pf, device=dev)
+    code = 1  # bf16 inputs
+    ws_bytes = binding.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    d = inputs.make_workload(dc, device=dev)
+    S = d["S"]
+    N, steps = dc.B, dc.T
+    o_dec = torch.empty((N, dc.H, dc.dv), dtype=torch.float32, device=dev)
+    copy_src = copy_dst = None
+    if args.copy_calibration:
+        copy_src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)   # 1 GiB
+        copy_dst = torch.empty_like(copy_src)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs):
+        e = evs
+        e[0].record(stream)
+        binding.kda_chunk_prep(ins["q"], ins["k"], ins["g"], ins["beta"], dv, workspace=ws)
+        e[1].record(stream)
+        binding.kda_chunk_state_pass(ins["v"], ws, dk, ins["S0"], o=o, S_T=ST)
+        e[2].record(stream)
+        for s in range(steps):
+            e[3 + 2 * s].record(stream)
+            binding.kda_decode_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S, o=o_dec)
+            e[4 + 2 * s].record(stream)
+        if copy_src is not None:
+            copy_dst.copy_(copy_src)
+
+    nev = 3 + 2 * steps
+    new_events = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    all_ev = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(all_ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    prep_ms = np.array([e[0].elapsed_time(e[1]) for e in all_ev])
+    pass_ms = np.array([e[1].elapsed_time(e[2]) for e in all_ev])
+    dec_ms = np.array([[e[3 + 2 * s].elapsed_time(e[4 + 2 * s]) for s in range(steps)] for e in all_ev])
+    prefill_ms = prep_ms + pass_ms
+    tokens = B * T
+    value = tokens / (prefill_ms.mean() * 1e-3)
+
+    # ---- rooflines (algorithmic work / measured average launch time) ----
+    th = B * T * H
+    f_tok, b_tok = prefill_units(B, T, H, dk, dv)
+    state_bytes = 2 * dk * dv * 4                         # S_T write + S0 read
+    prep_bytes = th * (2 * 3 * dk + 2)                    # q, k, g, beta in
+    pass_bytes = th * (2 * dv + 4 * dv) + B * H * dk * dv * 4  # v in, o out, S_T out (S0 = 0)
+    path_bytes = th * b_tok + B * H * dk * dv * 4
+    dec_unit_bytes = state_bytes + 2 * (3 * dc.dk + dc.dv) + 2 + 4 * dc.dv
+    dec_bytes = N * dc.H * dec_unit_bytes
+    dec_state_bytes = N * dc.H * state_bytes
+
+    def roof(name, nbytes, ms, sources, bound="hbm"):
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        traffic = load_traffic(name)
+        return {"kernel": name, "bound": bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "algorithmic_bytes_per_launch": int(nbytes),
+                "avg_launch_us": round(ms * 1e3, 2)}
+
+    r_dec = roof("kda_decode_kernel", dec_bytes, dec_ms.mean(), ["linear_attention_recurrence_11_amd/csrc/kda_decode.hip"])
+    r_prep = roof("kda_chunk_prep", prep_bytes, prep_ms.mean(), ["linear_attention_recurrence_11_amd/csrc/kda_chunk.hip"])
+    r_pass = roof("kda_state_pass", pass_bytes, pass_ms.mean(), ["linear_attention_recurrence_11_amd/csrc/kda_chunk.hip"])
+    step_share = {"kda_decode_kernel": dec_ms.sum(1).mean(), "kda_chunk_prep": prep_ms.mean(),
+                  "kda_state_pass": pass_ms.mean()}
+    dominant = max(step_share, key=step_share.get)
+    roofs = {"kda_decode_kernel": r_dec, "kda_chunk_prep": r_prep, "kda_state_pass": r_pass}
+    prefill_gbps = path_bytes / (prefill_ms.mean() * 1e-3) / 1e9
+    prefill_tflops = th * f_tok / (prefill_ms.mean() * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": pf.name, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": 16,
+                   "in_dtype": "bf16", "state_dtype": "f32", "out_dtype": "f32",
+                   "decode_workload": dc.name, "decode_requests": N, "decode_steps": steps},
+        "roofline": roofs[dominant],
+        "prefill": {
+            "tokens_per_s": round(value, 1), "ms": round(prefill_ms.mean(), 4),
+            "prep_ms": round(prep_ms.mean(), 4), "state_pass_ms": round(pass_ms.mean(), 4),
+            "algorithmic_GBps": round(prefill_gbps, 1),
+            "frac_of_hbm_roof": round(prefill_gbps / HBM_PEAK_GBPS, 4),
+            "algorithmic_TFLOPs": round(prefill_tflops, 2),
+            "frac_of_bf16_mfma_peak": round(prefill_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "bytes_per_token_head": b_tok, "flops_per_token_head": f_tok,
+        },
+        "decode": {
+            "state_GBps": round(dec_state_bytes / (dec_ms.mean() * 1e-3) / 1e9, 1),
+            "all_GBps": round(dec_bytes / (dec_ms.mean() * 1e-3) / 1e9, 1),
+            "frac_of_hbm_roof": round(dec_bytes / (dec_ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "us_per_step": round(dec_ms.mean() * 1e3, 2), "steps_per_launch_set": steps,
+        },
+        "kernels": roofs,
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"], rec["sampled_parity"] = cpu_leg(ins, o, args.cpu_tokens, pf)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_leg(ins, o, ntok, pf):
+    """The fp64 oracle (test infrastructure) on the first `ntok` tokens of all
+    heads of the prefill workload, timed on this host's cores; its outputs also
+    check the GPU outputs for those tokens."""
+    import numpy as np
+
+    from linear_attention_recurrence_11_amd import inputs
+    from oracle import c_oracle
+
+    ntok = min(ntok, pf.T)
+    to = inputs.to_oracle
+    host = {n: to(ins[n][:, :ntok].contiguous()) for n in ("q", "k", "v", "g", "beta")}
+    threads = c_oracle.default_threads()
+    print("[bench] oracle on %d tokens x %d heads, %d threads" % (ntok, pf.H, threads),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    o_ref, _ = c_oracle.fwd(host["q"], host["k"], host["v"], host["g"], host["beta"], None,
+                            nthreads=threads, want_state=False)
+    wall = time.perf_counter() - t0
+    og = o[:, :ntok].float().cpu().numpy()
+    err = float(np.abs(og - o_ref).max() / np.sqrt(np.mean(o_ref ** 2)))
+    base = {"value": round(pf.B * ntok / wall, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "wall_s": round(wall, 2),
+            "sample": "fp64 C oracle, first %d of %d tokens, all %d heads of %s" % (ntok, pf.T, pf.H, pf.name)}
+    parity = {"err_o_max_over_rms": err, "tokens": ntok, "heads": pf.H, "tolerance": 2e-2}
+    return base, parity
+
+
+if __name__ == "__main__":
+    main()

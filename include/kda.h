@@ -120,6 +120,33 @@ kda_status kda_chunk_fwd_check(const void* q, const void* k, const void* v,
                                size_t workspace_bytes);
 
 /*
+ * The two stages kda_chunk_fwd runs, exposed separately (same arguments and
+ * rules as kda_chunk_fwd). kda_chunk_fwd(...) is exactly kda_chunk_prep then
+ * kda_chunk_state_pass on the same stream.
+ *
+ * kda_chunk_prep: every 16-token chunk of every (b, h) independently — the
+ * per-chunk cumulative log-decay, the decay-scaled query and key operands, the
+ * chunk Gram tiles, (I + strictly_lower(diag(beta) Kt Kh^T))^-1 and the
+ * products the state pass needs — written to `workspace`. Reads q, k, g, beta
+ * only; the workspace then depends on nothing else, so one prep can feed
+ * several state passes (e.g. replays of the same tokens from different
+ * initial states, where only S0 and v change).
+ *
+ * kda_chunk_state_pass: the sequential pass over the chunks of each (b, h)
+ * from S0, reading v and the workspace written by kda_chunk_prep for the same
+ * B, T, H, dk, dv and in_dtype; writes o and S_T.
+ */
+kda_status kda_chunk_prep(const void* q, const void* k, const void* g, const void* beta,
+                          int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                          int in_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+kda_status kda_chunk_state_pass(const void* v, const void* workspace,
+                                size_t workspace_bytes, const float* S0, void* o,
+                                float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                int64_t dv, int in_dtype, int out_dtype, void* stream);
+
+/*
  * One decode step: one token for each of N independent requests, updating
  * each request's state in place.
  *

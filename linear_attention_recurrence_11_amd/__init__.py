@@ -5,5 +5,5 @@ The compute path is the C-ABI library libkda.so (hand-written HIP kernels);
 the library is opened on first use and its absence is an error.
 """
 from .binding import (KDAError, kda_abi_version, kda_chunk_fwd,  # noqa: F401
-                      kda_chunk_fwd_workspace_size, kda_decode_step, kda_status_str,
-                      library_path)
+                      kda_chunk_fwd_workspace_size, kda_chunk_prep, kda_chunk_state_pass,
+                      kda_decode_step, kda_status_str, library_path)

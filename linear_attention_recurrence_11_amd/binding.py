@@ -47,6 +47,10 @@ def _load():
         lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i64] * 5 + [i, i, vp, sz, vp]
         lib.kda_chunk_fwd_check.restype = i
         lib.kda_chunk_fwd_check.argtypes = [vp] * 8 + [i64] * 5 + [i, i, vp, sz]
+        lib.kda_chunk_prep.restype = i
+        lib.kda_chunk_prep.argtypes = [vp] * 4 + [i64] * 5 + [i, vp, sz, vp]
+        lib.kda_chunk_state_pass.restype = i
+        lib.kda_chunk_state_pass.argtypes = [vp, vp, sz, vp, vp, vp] + [i64] * 5 + [i, i, vp]
         lib.kda_decode_step.restype = i
         lib.kda_decode_step.argtypes = [vp] * 7 + [i64] * 4 + [i, i, vp]
         lib.kda_decode_step_check.restype = i
@@ -121,6 +125,43 @@ def kda_chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, out_dtype=torc
                            wbytes, _stream(stream, dev))
     if st != _STATUS_OK:
         raise KDAError(st, "kda_chunk_fwd")
+    return o, S_T
+
+
+def kda_chunk_prep(q, k, g, beta, dv, *, workspace=None, stream=None):
+    """First stage of kda_chunk_fwd: per-chunk operands into a workspace
+    (allocated here when not given). Returns the workspace tensor."""
+    lib = _load()
+    B, T, H, dk = q.shape
+    code = _dcode(q.dtype)
+    need = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), B, T, H, dk, dv, code,
+                            _ptr(workspace), wbytes, _stream(stream, q.device))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_chunk_prep")
+    return workspace
+
+
+def kda_chunk_state_pass(v, workspace, dk, S0=None, *, o=None, S_T=None, in_dtype=None,
+                         out_dtype=torch.float32, want_state=True, stream=None):
+    """Second stage of kda_chunk_fwd: the sequential pass from S0 over the chunks
+    prepared in `workspace` (by kda_chunk_prep on the same sizes and in_dtype)."""
+    lib = _load()
+    B, T, H, dv = v.shape
+    code = _dcode(v.dtype if in_dtype is None else in_dtype)
+    dev = v.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_state_pass(_ptr(v), _ptr(workspace), wbytes, _ptr(S0), _ptr(o), _ptr(S_T),
+                                  B, T, H, dk, dv, code, _dcode(o.dtype), _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_chunk_state_pass")
     return o, S_T
 
 

@@ -59,11 +59,26 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
   return static_cast<size_t>(B * H * NC * L.bytes);
 }
 
-kda_status kda_chunk_fwd_check(const void* q, const void* k, const void* v, const void* g,
-                               const void* beta, const float* S0, const void* o,
-                               const float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk,
-                               int64_t dv, int in_dtype, int out_dtype, const void* workspace,
-                               size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+enum : unsigned { kPrep = 1u, kPass = 2u };
+
+struct ChunkPtrs {
+  const void *q, *k, *v, *g, *beta;
+  const float* S0;
+  const void* o;
+  const float* S_T;
+  const void* ws;
+  size_t ws_bytes;
+};
+
+// The argument rules of include/kda.h for the tensors a stage touches:
+// kPrep reads q, k, g, beta and writes the workspace; kPass reads v, S0 and
+// the workspace and writes o and S_T.
+kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                       int in_dtype, int out_dtype, unsigned stages) {
   if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return KDA_ERR_SHAPE;
   if (B > kMaxElems || T > kMaxElems || H > kMaxElems) return KDA_ERR_SHAPE;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
@@ -75,50 +90,93 @@ kda_status kda_chunk_fwd_check(const void* q, const void* k, const void* v, cons
   if (B * H * NC > 0x7fffffffLL || B * H > 0x0fffffffLL) return KDA_ERR_UNSUPPORTED;
   const int64_t BH = B * H, BTH = B * T * H;
   if (BH == 0) return KDA_OK;  // nothing to read or write
-  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
+  const bool prep = stages & kPrep, pass = stages & kPass;
+  if (T > 0 && prep && (!p.q || !p.k || !p.g || !p.beta)) return KDA_ERR_NULL;
+  if (T > 0 && pass && (!p.v || !p.o)) return KDA_ERR_NULL;
   const size_t need = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype);
-  if (T > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
-  const int64_t es = dsize(in_dtype);
-  {
-    const void* vec4[] = {q, k, g};  // read as 4-element vectors
-    for (const void* p : vec4)
-      if (p && !aligned(p, 4 * es)) return KDA_ERR_ALIGNMENT;
-    const void* elem[] = {v, beta};
-    for (const void* p : elem)
-      if (p && !aligned(p, es)) return KDA_ERR_ALIGNMENT;
-    if ((o && !aligned(o, dsize(out_dtype))) || (S0 && !aligned(S0, 4)) || (S_T && !aligned(S_T, 4)))
-      return KDA_ERR_ALIGNMENT;
-    if (T > 0 && workspace && !aligned(workspace, 16)) return KDA_ERR_ALIGNMENT;
+  if (T > 0 && (!p.ws || p.ws_bytes < need)) return KDA_ERR_WORKSPACE;
+  const int64_t es = dsize(in_dtype), eo = dsize(out_dtype);
+  if (prep) {
+    const void* vec4[] = {p.q, p.k, p.g};  // read as 4-element vectors
+    for (const void* x : vec4)
+      if (x && !aligned(x, 4 * es)) return KDA_ERR_ALIGNMENT;
+    if (p.beta && !aligned(p.beta, es)) return KDA_ERR_ALIGNMENT;
   }
-  const Range rq = range_of(q, BTH * dk, es), rk = range_of(k, BTH * dk, es);
-  const Range rv = range_of(v, BTH * dv, es), rg = range_of(g, BTH * dk, es);
-  const Range rb = range_of(beta, BTH, es);
-  const Range rs0 = range_of(S0, S0 ? BH * dk * dv : 0, 4);
-  const Range ro = range_of(o, BTH * dv, dsize(out_dtype));
-  const Range rst = range_of(S_T, S_T ? BH * dk * dv : 0, 4);
-  const Range rw = range_of(workspace, T > 0 && workspace ? static_cast<int64_t>(need) : 0, 1);
-  const Range inputs[] = {rq, rk, rv, rg, rb};
-  for (const Range& x : inputs) {
-    if (T > 0 && overlap(ro, x)) return KDA_ERR_ALIAS;
-    if (overlap(rst, x) || overlap(rw, x)) return KDA_ERR_ALIAS;
+  if (pass) {
+    if ((p.v && !aligned(p.v, es)) || (p.o && !aligned(p.o, eo))) return KDA_ERR_ALIGNMENT;
+    if ((p.S0 && !aligned(p.S0, 4)) || (p.S_T && !aligned(p.S_T, 4))) return KDA_ERR_ALIGNMENT;
   }
-  if (T > 0 && (overlap(ro, rs0) || overlap(ro, rst) || overlap(ro, rw))) return KDA_ERR_ALIAS;
-  if (overlap(rw, rs0) || overlap(rw, rst)) return KDA_ERR_ALIAS;
-  if (overlap(rst, rs0) && S_T != S0) return KDA_ERR_ALIAS;
+  if (T > 0 && !aligned(p.ws, 16)) return KDA_ERR_ALIGNMENT;
+  const Range none{0, 0};
+  const Range rq = prep ? range_of(p.q, BTH * dk, es) : none;
+  const Range rk = prep ? range_of(p.k, BTH * dk, es) : none;
+  const Range rg = prep ? range_of(p.g, BTH * dk, es) : none;
+  const Range rb = prep ? range_of(p.beta, BTH, es) : none;
+  const Range rv = pass ? range_of(p.v, BTH * dv, es) : none;
+  const Range rs0 = pass && p.S0 ? range_of(p.S0, BH * dk * dv, 4) : none;
+  const Range ro = pass && T > 0 ? range_of(p.o, BTH * dv, eo) : none;
+  const Range rst = pass && p.S_T ? range_of(p.S_T, BH * dk * dv, 4) : none;
+  const Range rw = T > 0 ? range_of(p.ws, static_cast<int64_t>(need), 1) : none;
+  const Range ins[] = {rq, rk, rv, rg, rb, rs0};
+  for (const Range& x : ins) {
+    if (overlap(ro, x) || overlap(rw, x)) return KDA_ERR_ALIAS;
+    if (&x != &ins[5] && overlap(rst, x)) return KDA_ERR_ALIAS;
+  }
+  if (overlap(ro, rst) || overlap(ro, rw) || overlap(rw, rst)) return KDA_ERR_ALIAS;
+  if (overlap(rst, rs0) && p.S_T != p.S0) return KDA_ERR_ALIAS;
   return KDA_OK;
+}
+
+kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_check(const void* q, const void* k, const void* v, const void* g,
+                               const void* beta, const float* S0, const void* o,
+                               const float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk,
+                               int64_t dv, int in_dtype, int out_dtype, const void* workspace,
+                               size_t workspace_bytes) {
+  const ChunkPtrs p{q, k, v, g, beta, S0, o, S_T, workspace, workspace_bytes};
+  return check_chunk(p, B, T, H, dk, dv, in_dtype, out_dtype, kPrep | kPass);
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const float* S0, void* o, float* S_T, int64_t B,
                          int64_t T, int64_t H, int64_t dk, int64_t dv, int in_dtype, int out_dtype,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  const kda_status st = kda_chunk_fwd_check(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
-                                            in_dtype, out_dtype, workspace, workspace_bytes);
+  const ChunkPtrs p{q, k, v, g, beta, S0, o, S_T, workspace, workspace_bytes};
+  const kda_status st = check_chunk(p, B, T, H, dk, dv, in_dtype, out_dtype, kPrep | kPass);
   if (st != KDA_OK) return st;
   if (B * H == 0) return KDA_OK;
   kda::ChunkFwdArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype, workspace};
-  const hipError_t e = kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_chunk_prep(const void* q, const void* k, const void* g, const void* beta,
+                          int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const ChunkPtrs p{q, k, nullptr, g, beta, nullptr, nullptr, nullptr, workspace, workspace_bytes};
+  const kda_status st = check_chunk(p, B, T, H, dk, dv, in_dtype, KDA_F32, kPrep);
+  if (st != KDA_OK) return st;
+  if (B * H == 0 || T == 0) return KDA_OK;
+  kda::ChunkFwdArgs a{q, k, nullptr, g, beta, nullptr, nullptr, nullptr, B, T, H, dk, dv,
+                      in_dtype, KDA_F32, workspace};
+  return launch_status(kda::launch_chunk_prep(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_chunk_state_pass(const void* v, const void* workspace, size_t workspace_bytes,
+                                const float* S0, void* o, float* S_T, int64_t B, int64_t T,
+                                int64_t H, int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                                void* stream) {
+  const ChunkPtrs p{nullptr, nullptr, v, nullptr, nullptr, S0, o, S_T, workspace, workspace_bytes};
+  const kda_status st = check_chunk(p, B, T, H, dk, dv, in_dtype, out_dtype, kPass);
+  if (st != KDA_OK) return st;
+  if (B * H == 0) return KDA_OK;
+  kda::ChunkFwdArgs a{nullptr, nullptr, v, nullptr, nullptr, S0, o, S_T, B, T, H, dk, dv,
+                      in_dtype, out_dtype, const_cast<void*>(workspace)};
+  return launch_status(kda::launch_chunk_state_pass(a, static_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_decode_step_check(const void* q, const void* k, const void* v, const void* g,

@@ -477,49 +477,72 @@ __global__ void kda_copy_state(const float* S0, float* ST, int64_t n) {
   if (i < n) ST[i] = S0 ? S0[i] : 0.f;
 }
 
-template <typename InT, typename OutT, int DK>
-hipError_t launch_typed(const ChunkFwdArgs& a, hipStream_t stream) {
-  constexpr bool F32 = Path<InT>::kF32;
-  const RecordLayout L = record_layout(DK, F32);
+template <typename InT, int DK>
+hipError_t launch_prep_typed(const ChunkFwdArgs& a, hipStream_t stream) {
+  const RecordLayout L = record_layout(DK, Path<InT>::kF32);
   const int64_t NC = (a.T + 15) / 16;
-  const int64_t nheads = a.B * a.H;
-  const int64_t prep_blocks = a.B * NC * a.H;
-  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  hipLaunchKernelGGL((kda_chunk_prep<InT, DK>), dim3(static_cast<uint32_t>(prep_blocks)), dim3(64),
-                     0, stream, static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
-                     static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta), ws, a.T, a.H,
-                     NC, L);
-  const int64_t nslices = a.dv / 16;
-  const int64_t groups = (nheads + 7) / 8;
-  const int64_t pass_blocks = 8 * nslices * groups;
-  hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(pass_blocks)),
-                     dim3(64), 0, stream, static_cast<const InT*>(a.v), ws, a.S0,
-                     static_cast<OutT*>(a.o), a.S_T, a.T, a.H, a.dv, NC, nslices, nheads, L);
+  const int64_t blocks = a.B * NC * a.H;
+  hipLaunchKernelGGL((kda_chunk_prep<InT, DK>), dim3(static_cast<uint32_t>(blocks)), dim3(64), 0,
+                     stream, static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
+                     static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta),
+                     static_cast<uint8_t*>(a.workspace), a.T, a.H, NC, L);
   return hipGetLastError();
 }
 
+template <typename InT, typename OutT, int DK>
+hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
+  const RecordLayout L = record_layout(DK, Path<InT>::kF32);
+  const int64_t NC = (a.T + 15) / 16;
+  const int64_t nheads = a.B * a.H;
+  const int64_t nslices = a.dv / 16;
+  const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
+  hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(blocks)), dim3(64),
+                     0, stream, static_cast<const InT*>(a.v),
+                     static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
+                     a.S_T, a.T, a.H, a.dv, NC, nslices, nheads, L);
+  return hipGetLastError();
+}
+
+template <typename InT>
+hipError_t launch_prep_dk(const ChunkFwdArgs& a, hipStream_t s) {
+  return a.dk == 64 ? launch_prep_typed<InT, 64>(a, s) : launch_prep_typed<InT, 128>(a, s);
+}
+
 template <typename InT, typename OutT>
-hipError_t launch_dk(const ChunkFwdArgs& a, hipStream_t s) {
-  return a.dk == 64 ? launch_typed<InT, OutT, 64>(a, s) : launch_typed<InT, OutT, 128>(a, s);
+hipError_t launch_pass_dk(const ChunkFwdArgs& a, hipStream_t s) {
+  return a.dk == 64 ? launch_pass_typed<InT, OutT, 64>(a, s) : launch_pass_typed<InT, OutT, 128>(a, s);
+}
+
+// T = 0: S_T is S0 (or zeros) unless it is S0 itself.
+hipError_t launch_empty(const ChunkFwdArgs& a, hipStream_t stream) {
+  if (a.S_T && a.S_T != a.S0) {
+    const int64_t n = a.B * a.H * a.dk * a.dv;
+    hipLaunchKernelGGL(kda_copy_state, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                       stream, a.S0, a.S_T, n);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream) {
-  const int64_t nheads = a.B * a.H;
-  if (nheads == 0) return hipSuccess;
-  if (a.T == 0) {
-    if (a.S_T && a.S_T != a.S0) {
-      const int64_t n = nheads * a.dk * a.dv;
-      hipLaunchKernelGGL(kda_copy_state, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
-                         stream, a.S0, a.S_T, n);
-      return hipGetLastError();
-    }
-    return hipSuccess;
-  }
+hipError_t launch_chunk_prep(const ChunkFwdArgs& a, hipStream_t stream) {
+  if (a.B * a.H == 0 || a.T == 0) return hipSuccess;
+  return a.in_dtype == 0 ? launch_prep_dk<float>(a, stream) : launch_prep_dk<uint16_t>(a, stream);
+}
+
+hipError_t launch_chunk_state_pass(const ChunkFwdArgs& a, hipStream_t stream) {
+  if (a.B * a.H == 0) return hipSuccess;
+  if (a.T == 0) return launch_empty(a, stream);
   const bool in32 = a.in_dtype == 0, out32 = a.out_dtype == 0;
-  if (in32) return out32 ? launch_dk<float, float>(a, stream) : launch_dk<float, uint16_t>(a, stream);
-  return out32 ? launch_dk<uint16_t, float>(a, stream) : launch_dk<uint16_t, uint16_t>(a, stream);
+  if (in32) return out32 ? launch_pass_dk<float, float>(a, stream) : launch_pass_dk<float, uint16_t>(a, stream);
+  return out32 ? launch_pass_dk<uint16_t, float>(a, stream) : launch_pass_dk<uint16_t, uint16_t>(a, stream);
+}
+
+hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream) {
+  const hipError_t e = launch_chunk_prep(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_chunk_state_pass(a, stream);
 }
 
 }  // namespace kda

@@ -54,6 +54,9 @@ struct DecodeArgs {
 
 // Launch the chunkwise forward (prep kernel then state pass) on `stream`.
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream);
+// The two stages on their own (fields of `a` a stage does not use are ignored).
+hipError_t launch_chunk_prep(const ChunkFwdArgs& a, hipStream_t stream);
+hipError_t launch_chunk_state_pass(const ChunkFwdArgs& a, hipStream_t stream);
 
 // Launch one decode step on `stream`.
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);

@@ -167,3 +167,26 @@ def test_decode_check(lib):
     assert call([None] * 7, N=0) == OK
     st = lib.kda_decode_step(*[vp(x) for x in a[:6]], vp(a[5]), N, H, dk, dv, BF16, F32, None)
     assert st == ALIAS
+
+
+def test_stage_entry_points_check_their_own_tensors(lib):
+    p, sz = fake_chunk()
+    B, T, H, dk, dv, ind, outd = sz
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    prep = lambda **o: lib.kda_chunk_prep(
+        vp(o.get("q", p["q"])), vp(p["k"]), vp(p["g"]), vp(p["beta"]), B, o.get("T", T), H, dk, dv,
+        ind, vp(o.get("ws", p["ws"])), o.get("ws_bytes", p["ws_bytes"]), None)
+    passf = lambda **o: lib.kda_chunk_state_pass(
+        vp(o.get("v", p["v"])), vp(o.get("ws", p["ws"])), p["ws_bytes"], vp(p["S0"]),
+        vp(o.get("o", p["o"])), vp(o.get("S_T", p["S_T"])), B, T, H, dk, dv, ind, outd, None)
+    assert prep(q=None) == NULL
+    assert prep(ws=None) == WS
+    assert prep(ws_bytes=p["ws_bytes"] - 16) == WS
+    assert prep(ws=p["q"]) == ALIAS
+    assert prep(q=p["q"] + 4) == ALIGN
+    assert prep(T=0, ws=None, ws_bytes=0) == OK       # nothing to do, no launch
+    assert passf(v=None) == NULL
+    assert passf(o=p["v"]) == ALIAS
+    assert passf(ws=p["o"]) == ALIAS
+    assert passf(S_T=p["S0"] + 128) == ALIAS
+    assert passf(v=p["v"] + 2) == ALIGN

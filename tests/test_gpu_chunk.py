@@ -192,3 +192,21 @@ def test_nan_propagates_from_its_chunk():
     assert bool(torch.isfinite(o[0, :32]).all())
     assert bool(torch.isnan(o[0, 37:]).all())
     assert bool(torch.isnan(ST).any())
+
+
+def test_stages_equal_forward_and_prep_is_reusable():
+    """kda_chunk_prep + kda_chunk_state_pass is bit-identical to kda_chunk_fwd,
+    and one prep serves passes from different initial states."""
+    ins = inputs.make_forward(2, 150, 3, 128, 64, "bf16", "normal", seed=27, device=DEV)
+    announce("stages")
+    o_ref, S_ref = gpu_forward(ins)
+    ws = binding.kda_chunk_prep(ins["q"], ins["k"], ins["g"], ins["beta"], 64)
+    o1, S1 = binding.kda_chunk_state_pass(ins["v"], ws, 128, ins["S0"])
+    S0b = torch.randn_like(ins["S0"]) * 0.02
+    o2, S2 = binding.kda_chunk_state_pass(ins["v"], ws, 128, S0b)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o_ref) and torch.equal(S1, S_ref)
+    ins2 = dict(ins)
+    ins2["S0"] = S0b
+    o_ref2, S_ref2 = gpu_forward(ins2)
+    assert torch.equal(o2, o_ref2) and torch.equal(S2, S_ref2)

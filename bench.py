@@ -205,6 +205,22 @@ def main():
         "kernels": roofs,
     }
 
+    # practical HBM ceiling for context: a plain device-to-device copy
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    cev[0].record(stream)
+    for i in range(5):
+        dst.copy_(src)
+        cev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = np.mean([cev[i].elapsed_time(cev[i + 1]) for i in range(5)])
+    rec["hbm_copy_reference"] = {"bytes": 2 * src.numel() * 4, "ms": round(copy_ms, 4),
+                                 "GBps": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1)}
+    del src, dst
+
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["sampled_parity"] = cpu_leg(ins, o, args.cpu_tokens, pf)
     print(json.dumps(rec), flush=True)

@@ -27,8 +27,9 @@
  *    (hipMalloc'd or equivalent). The library allocates nothing and keeps no
  *    global state; calls are re-entrant and may run on any stream.
  *  - Tensors are dense, row-major, packed (no strides). Alignment: q, k, g
- *    to 4 elements (16 bytes for fp32, 8 bytes for bf16); the workspace and
- *    the decode state S to 16 bytes; every other tensor to its element size.
+ *    to 4 elements (16 bytes for fp32, 8 bytes for bf16); the forward's v,
+ *    the workspace and the decode state S to 16 bytes; every other tensor to
+ *    its element size.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *    All argument checks happen on the host before anything is launched; on
  *    any error nothing is launched and no output is written.
@@ -91,7 +92,8 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
  *            not read before it is written; contents after the call are
  *            unspecified. Must not overlap any tensor.
  *
- * Supported: dk in {64, 128}; dv a multiple of 16 in [16, 512]; B, H >= 0;
+ * Supported: dk in {64, 128}; dv a multiple of 16 in [16, 512]; B, H >= 0
+ * with H * dv <= 2^25;
  * T >= 0 (T = 0 copies S0, or zeros, into S_T). in_dtype KDA_F32 (all fp32
  * arithmetic, fp32 matrix-core products) or KDA_BF16 (bf16 inputs; bf16
  * split-precision chunk Gram products, fp16 state products, fp32

@@ -32,6 +32,9 @@ def build(verbose=False, extra_flags=()):
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            "-I" + INCLUDE, "-I" + CSRC,
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # keep matrix-core accumulators in VGPRs: the state pass feeds them
+           # to VALU work every chunk, and AGPR residency costs a move each way
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wno-unused-command-line-argument"]
     cmd += list(extra_flags)
     cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]

@@ -88,6 +88,7 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
   if (toks * (dk > dv ? dk : dv) > static_cast<double>(kMaxElems)) return KDA_ERR_SHAPE;
   const int64_t NC = (T + 15) / 16;
   if (B * H * NC > 0x7fffffffLL || B * H > 0x0fffffffLL) return KDA_ERR_UNSUPPORTED;
+  if (H * dv > (int64_t(1) << 25)) return KDA_ERR_UNSUPPORTED;  // 32-bit per-lane offsets
   const int64_t BH = B * H, BTH = B * T * H;
   if (BH == 0) return KDA_OK;  // nothing to read or write
   const bool prep = stages & kPrep, pass = stages & kPass;
@@ -103,7 +104,7 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
     if (p.beta && !aligned(p.beta, es)) return KDA_ERR_ALIGNMENT;
   }
   if (pass) {
-    if ((p.v && !aligned(p.v, es)) || (p.o && !aligned(p.o, eo))) return KDA_ERR_ALIGNMENT;
+    if ((p.v && !aligned(p.v, 16)) || (p.o && !aligned(p.o, eo))) return KDA_ERR_ALIGNMENT;
     if ((p.S0 && !aligned(p.S0, 4)) || (p.S_T && !aligned(p.S_T, 4))) return KDA_ERR_ALIGNMENT;
   }
   if (T > 0 && !aligned(p.ws, 16)) return KDA_ERR_ALIGNMENT;

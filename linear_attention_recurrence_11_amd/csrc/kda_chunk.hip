@@ -304,13 +304,14 @@ struct ChunkFrags {
   f32x4 eg[NM];
   float vv[4];
 
-  __device__ __forceinline__ void load(const uint8_t* rec, const RecordLayout& L, int l, int gq,
-                                       const InT* v, size_t vbase, int64_t tok0, int64_t T,
-                                       int64_t H, int64_t DV) {
+  // Record fragments of one chunk; `rec` is uniform across the wavefront, so
+  // every address is a scalar base plus a fixed per-lane offset.
+  __device__ __forceinline__ void load_record(const uint8_t* rec, const RecordLayout& L, int l,
+                                              int gq) {
     if constexpr (F32) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const size_t off = static_cast<size_t>(m * 64 + l) * 16;
+        const uint32_t off = static_cast<uint32_t>(m * 64 + l) * 16;
         w[m] = *reinterpret_cast<const f32x4*>(rec + L.w + off);
         q[m] = *reinterpret_cast<const f32x4*>(rec + L.q + off);
         kb[m] = *reinterpret_cast<const f32x4*>(rec + L.kbar + off);
@@ -320,13 +321,13 @@ struct ChunkFrags {
     } else {
 #pragma unroll
       for (int p = 0; p < NM / 2; ++p) {
-        const size_t off = static_cast<size_t>(p * 64 + l) * 16;
+        const uint32_t off = static_cast<uint32_t>(p * 64 + l) * 16;
         w[p] = *reinterpret_cast<const f16x8*>(rec + L.w + off);
         q[p] = *reinterpret_cast<const f16x8*>(rec + L.q + off);
       }
 #pragma unroll
       for (int m = 0; m < NM; ++m)
-        kb[m] = *reinterpret_cast<const f16x4*>(rec + L.kbar + static_cast<size_t>(m * 64 + l) * 8);
+        kb[m] = *reinterpret_cast<const f16x4*>(rec + L.kbar + static_cast<uint32_t>(m * 64 + l) * 8);
       mh = *reinterpret_cast<const f16x4*>(rec + L.m + l * 8);
       ml = *reinterpret_cast<const f16x4*>(rec + L.m + 512 + l * 8);
       tb = *reinterpret_cast<const f16x4*>(rec + L.tb + l * 8);
@@ -334,13 +335,94 @@ struct ChunkFrags {
     const f32x4* egp = reinterpret_cast<const f32x4*>(rec + L.eg) + gq * NM;
 #pragma unroll
     for (int m = 0; m < NM; ++m) eg[m] = egp[m];
+  }
+
+  // V rows 4gq + i of a chunk; `vchunk` (uniform) points at the chunk's first
+  // token of this (b, h), voff[i] = (4gq + i) * H * DV + col. Tokens at or
+  // past `valid` (a last partial chunk) read as zero.
+  __device__ __forceinline__ void load_v(const InT* vchunk, const uint32_t voff[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = tok0 + 4 * gq + i;
-      vv[i] = (t < T) ? load_in(v, vbase + static_cast<size_t>(t * H) * DV) : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) vv[i] = load_in(vchunk, voff[i]);
+  }
+  __device__ __forceinline__ void load_v_partial(const InT* vchunk, const uint32_t voff[4], int gq,
+                                                 int valid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = (4 * gq + i < valid) ? load_in(vchunk, voff[i]) : 0.f;
   }
 };
+
+// One chunk of the sequential pass on a dk x 16 state slice S (output layout):
+// U = Tb V - W S,  O = Qt S + M U,  S <- Diag(e^gamma) S + Kb^T U.  Returns O.
+template <typename InT, int DK>
+__device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<InT, DK>& cur, f32x4 (&S)[DK / 16]) {
+  constexpr int NM = DK / 16;
+  f32x4 U, O;
+  if constexpr (Path<InT>::kF32) {
+    U = zero4();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) U = mma_16x16x4_f32(cur.tb[i], cur.vv[i], U);   // Ut = Tb V
+    O = zero4();
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        U = mma_16x16x4_f32(cur.w[m][i], S[m][i], U);                        // U = Ut - W S
+        O = mma_16x16x4_f32(cur.q[m][i], S[m][i], O);                        // O = Qt S
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O = mma_16x16x4_f32(cur.mh[i], U[i], O);      // O += M U
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      S[m] = S[m] * cur.eg[m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[m] = mma_16x16x4_f32(cur.kb[m][i], U[i], S[m]);
+    }
+  } else {
+    // Every accumulation chain below uses one MFMA shape (16x16x32). Two shapes
+    // chained through an accumulator need wait states on gfx950 that the
+    // compiler does not insert; the 16-deep token contractions are issued as
+    // 16x16x32 with the upper 16 slots zero (or, for M U, holding the
+    // low-order part of M against a second copy of U). K=16 and K=32 issue at
+    // the same rate on gfx950, so the padding costs nothing.
+    f16x8 tbz, vz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tbz[i] = cur.tb[i];
+      tbz[i + 4] = static_cast<_Float16>(0.f);
+      vz[i] = static_cast<_Float16>(cur.vv[i]);
+      vz[i + 4] = static_cast<_Float16>(0.f);
+    }
+    U = mma_16x16x32_f16(tbz, vz, zero4());                                    // Ut = Tb V
+    f16x8 sh[NM / 2];
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
+    O = zero4();
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      U = mma_16x16x32_f16(cur.w[p], sh[p], U);                                // U = Ut - W S
+      O = mma_16x16x32_f16(cur.q[p], sh[p], O);                                // O = Qt S
+    }
+    f16x8 uu, mhl;
+    f16x4 u4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 x = static_cast<_Float16>(U[i]);
+      uu[i] = x;
+      uu[i + 4] = x;
+      u4[i] = x;
+      mhl[i] = cur.mh[i];
+      mhl[i + 4] = cur.ml[i];
+    }
+    O = mma_16x16x32_f16(mhl, uu, O);                                          // O += (Mhi + Mlo) U
+    // S = Diag(e^gamma) S + Kb^T U: the accumulator input is the VALU product
+    // S * e^gamma, never another MFMA's output, so the 16x16x16 shape is safe.
+#pragma unroll
+    for (int m = 0; m < NM; ++m) S[m] = mma_16x16x16_f16(cur.kb[m], u4, S[m] * cur.eg[m]);
+  }
+  return O;
+}
 
 template <typename InT, typename OutT, int DK>
 __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
@@ -351,6 +433,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
                                                      int64_t nheads, RecordLayout L) {
   constexpr bool F32 = Path<InT>::kF32;
   constexpr int NM = DK / 16;
+  using Frags = ChunkFrags<InT, DK>;
   const int l = threadIdx.x, c16 = l & 15, gq = l >> 4;
 
   // XCD-aware numbering: workgroups are dealt round-robin to the 8 XCDs, so
@@ -373,95 +456,67 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
     for (int i = 0; i < 4; ++i)
       S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
 
+  // Uniform per-(b,h) bases; per-lane offsets fixed for the whole sequence.
   const uint8_t* rec0 = ws + static_cast<size_t>(head) * NC * L.bytes;
-  const size_t vbase = static_cast<size_t>(b * T * H + h) * DV + col;
+  const size_t hb = static_cast<size_t>(b * T * H + h) * DV;   // token 0 of (b, h)
+  const InT* vb = v + hb;
+  OutT* ob = o + hb;
+  const size_t chunk_elems = static_cast<size_t>(16 * H) * DV;
+  uint32_t toff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) toff[i] = static_cast<uint32_t>((4 * gq + i) * H * DV + col);
 
-  ChunkFrags<InT, DK> cur, nxt;
-  cur.load(rec0, L, l, gq, v, vbase, 0, T, H, DV);
-  for (int64_t n = 0; n < NC; ++n) {
-    if (n + 1 < NC) nxt.load(rec0 + static_cast<size_t>(n + 1) * L.bytes, L, l, gq, v, vbase,
-                             (n + 1) * 16, T, H, DV);
-    f32x4 U, O;
+  const int64_t NF = T / 16;  // full chunks
+  // Full chunks: records prefetched two chunks ahead (fp32 path: one) into
+  // fragment buffers whose roles rotate by unrolling (a register copy between
+  // buffers would force a wait for the loads in flight); the last full chunk
+  // is re-read past the end instead of branching around the load.
+  auto fetch = [&](Frags& f, int64_t c) __attribute__((always_inline)) {
+    c = c < NF - 1 ? c : NF - 1;
+    f.load_record(rec0 + static_cast<size_t>(c) * L.bytes, L, l, gq);
+    f.load_v(vb + static_cast<size_t>(c) * chunk_elems, toff);
+  };
+  auto finish = [&](int64_t n, f32x4 O) __attribute__((always_inline)) {
+    OutT* oc = ob + static_cast<size_t>(n) * chunk_elems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_out(oc, toff[i], O[i]);
+  };
+  if (NF > 0) {
+    Frags f0, f1, f2;
     if constexpr (F32) {
-      // Ut = Tb V
-      U = zero4();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U = mma_16x16x4_f32(cur.tb[i], cur.vv[i], U);
-      // U = Ut - W S ; O = Qt S
-      O = zero4();
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          U = mma_16x16x4_f32(cur.w[m][i], S[m][i], U);
-          O = mma_16x16x4_f32(cur.q[m][i], S[m][i], O);
-        }
-      // O += M U
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O = mma_16x16x4_f32(cur.mh[i], U[i], O);
-      // S = Diag(e^gamma) S + Kb^T U
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        S[m] = S[m] * cur.eg[m];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[m] = mma_16x16x4_f32(cur.kb[m][i], U[i], S[m]);
+      fetch(f0, 0);
+      for (int64_t n = 0; n < NF; n += 2) {
+        fetch(f1, n + 1);
+        finish(n, chunk_step(f0, S));
+        if (n + 1 >= NF) break;
+        fetch(f0, n + 2);
+        finish(n + 1, chunk_step(f1, S));
       }
     } else {
-      // Every accumulation chain below uses one MFMA shape (16x16x32). Two
-      // shapes chained through an accumulator need wait states on gfx950
-      // that the compiler does not insert; the 16-deep token contractions
-      // are therefore issued as 16x16x32 with the upper 16 slots zero (or,
-      // for M U, holding the low-order part of M against a second copy of U).
-      f16x8 tbz, vz;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tbz[i] = cur.tb[i];
-        tbz[i + 4] = static_cast<_Float16>(0.f);
-        vz[i] = static_cast<_Float16>(cur.vv[i]);
-        vz[i + 4] = static_cast<_Float16>(0.f);
-      }
-      U = mma_16x16x32_f16(tbz, vz, zero4());          // Ut = Tb V
-      f16x8 sh[NM / 2];
-#pragma unroll
-      for (int p = 0; p < NM / 2; ++p)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
-      O = zero4();
-#pragma unroll
-      for (int p = 0; p < NM / 2; ++p) {
-        U = mma_16x16x32_f16(cur.w[p], sh[p], U);      // U = Ut - W S
-        O = mma_16x16x32_f16(cur.q[p], sh[p], O);      // O = Qt S
-      }
-      f16x8 uu, uz, mhl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 x = static_cast<_Float16>(U[i]);
-        uu[i] = x;
-        uu[i + 4] = x;
-        uz[i] = x;
-        uz[i + 4] = static_cast<_Float16>(0.f);
-        mhl[i] = cur.mh[i];
-        mhl[i + 4] = cur.ml[i];
-      }
-      O = mma_16x16x32_f16(mhl, uu, O);                // O += (Mhi + Mlo) U
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {                   // S = Diag(e^gamma) S + Kb^T U
-        f16x8 kz;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kz[i] = cur.kb[m][i];
-          kz[i + 4] = static_cast<_Float16>(0.f);
-        }
-        S[m] = mma_16x16x32_f16(kz, uz, S[m] * cur.eg[m]);
+      fetch(f0, 0);
+      fetch(f1, 1);
+      for (int64_t n = 0; n < NF; n += 3) {
+        fetch(f2, n + 2);
+        finish(n, chunk_step(f0, S));
+        if (n + 1 >= NF) break;
+        fetch(f0, n + 3);
+        finish(n + 1, chunk_step(f1, S));
+        if (n + 2 >= NF) break;
+        fetch(f1, n + 4);
+        finish(n + 2, chunk_step(f2, S));
       }
     }
-    // o rows 4gq + i of this chunk, column col
+  }
+  if (NC > NF) {  // last partial chunk: padded tokens read as zero and are not stored
+    const int valid = static_cast<int>(T - NF * 16);
+    Frags f;
+    f.load_record(rec0 + static_cast<size_t>(NF) * L.bytes, L, l, gq);
+    f.load_v_partial(vb + static_cast<size_t>(NF) * chunk_elems, toff, gq, valid);
+    const f32x4 O = chunk_step(f, S);
+    OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = n * 16 + 4 * gq + i;
-      if (t < T) store_out(o, vbase + static_cast<size_t>(t * H) * DV, O[i]);
-    }
-    if (n + 1 < NC) cur = nxt;
+    for (int i = 0; i < 4; ++i)
+      if (4 * gq + i < valid) store_out(oc, toff[i], O[i]);
   }
   if (ST) {
 #pragma unroll
@@ -491,10 +546,10 @@ hipError_t launch_prep_typed(const ChunkFwdArgs& a, hipStream_t stream) {
 
 template <typename InT, typename OutT, int DK>
 hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
+  const int64_t nslices = a.dv / 16;
   const RecordLayout L = record_layout(DK, Path<InT>::kF32);
   const int64_t NC = (a.T + 15) / 16;
   const int64_t nheads = a.B * a.H;
-  const int64_t nslices = a.dv / 16;
   const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
   hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(blocks)), dim3(64),
                      0, stream, static_cast<const InT*>(a.v),

@@ -12,7 +12,8 @@ constexpr int64_t kChunkTokens = 16;
 
 // Per-(batch, head, chunk) workspace record written by the chunk-prep kernel
 // and read by the state-pass kernel. Offsets in bytes; total is a multiple of
-// 256. `es` is the element size of the matrix-core operands it holds (2 for
+// 1024 (whole units of 64 lanes x 16 bytes, the state pass's load granule).
+// `es` is the element size of the matrix-core operands it holds (2 for
 // the fp16 operands of the bf16-input path, 4 for the fp32 path).
 struct RecordLayout {
   int64_t es, w, q, kbar, m, tb, eg, bytes;
@@ -30,7 +31,7 @@ inline RecordLayout record_layout(int64_t dk, bool f32_path) {
   L.tb = L.m + msz;
   L.eg = L.tb + 256 * L.es;
   const int64_t end = L.eg + dk * 4;
-  L.bytes = (end + 255) / 256 * 256;
+  L.bytes = (end + 1023) / 1024 * 1024;  // whole 1 KiB units: 64 lanes x 16 bytes
   return L;
 }
 

@@ -44,12 +44,12 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # 16-token chunks; one record per (b, h, chunk): 14336 B (bf16 in, dk 128),
-    # 27136 B (fp32 in, dk 128)
+    # 16-token chunks; one record per (b, h, chunk), whole KiB: 14336 B (bf16 in,
+    # dk 128), 27648 B (fp32 in, dk 128), 15360 B (fp32 in, dk 64)
     assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == 32 * 4096 * 14336
     assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == 64 * 256 * 14336
-    assert binding.kda_chunk_fwd_workspace_size(1, 256, 2, 64, 64, F32) == 2 * 16 * 14592
-    assert binding.kda_chunk_fwd_workspace_size(1, 17, 1, 128, 128, F32) == 2 * 27136
+    assert binding.kda_chunk_fwd_workspace_size(1, 256, 2, 64, 64, F32) == 2 * 16 * 15360
+    assert binding.kda_chunk_fwd_workspace_size(1, 17, 1, 128, 128, F32) == 2 * 27648
     assert binding.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, F32) == 0
     assert binding.kda_chunk_fwd_workspace_size(1, 16, 1, 96, 128, F32) == 0
     assert binding.kda_chunk_fwd_workspace_size(1, 16, 1, 128, 24, F32) == 0
@@ -190,3 +190,4 @@ def test_stage_entry_points_check_their_own_tensors(lib):
     assert passf(ws=p["o"]) == ALIAS
     assert passf(S_T=p["S0"] + 128) == ALIAS
     assert passf(v=p["v"] + 2) == ALIGN
+    assert passf(v=p["v"] + 8) == ALIGN      # v: 16 bytes

@@ -63,8 +63,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--cpu-tokens", type=int, default=32768,
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens (all 32 heads) of the prefill workload the oracle runs")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the snapshot / speculative-decoding measurements (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -138,6 +140,10 @@ def main():
     pass_ms = np.array([e[1].elapsed_time(e[2]) for e in all_ev])
     dec_ms = np.array([[e[3 + 2 * s].elapsed_time(e[4 + 2 * s]) for s in range(steps)] for e in all_ev])
     prefill_ms = prep_ms + pass_ms
+
+    nxt = None
+    if not args.no_next:
+        nxt = measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, dev, np, torch)
     tokens = B * T
     value = tokens / (prefill_ms.mean() * 1e-3)
 
@@ -203,6 +209,7 @@ def main():
             "us_per_step": round(dec_ms.mean() * 1e3, 2), "steps_per_launch_set": steps,
         },
         "kernels": roofs,
+        "next": nxt,
     }
 
     # practical HBM ceiling for context: a plain device-to-device copy
@@ -224,6 +231,66 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["sampled_parity"] = cpu_leg(ins, o, args.cpu_tokens, pf)
     print(json.dumps(rec), flush=True)
+
+
+def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, dev, np, torch,
+                 reps=5, every=512, draft=4, accept=2):
+    """The options built on the path, timed after the steps with HIP events:
+    the prefill with a state snapshot every `every` tokens (prefix reuse), and
+    speculative verify of `draft` tokens + commit of `accept` of them for the
+    decode batch, against the decode steps they replace."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    snaps = torch.empty((B, T // every, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 1):
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if r:
+                ts.append(a.elapsed_time(b))
+        return float(np.mean(ts))
+
+    snap_ms = timed(lambda: binding.kda_chunk_fwd_ex(
+        ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"], snapshot_every=every,
+        snapshots=snaps, o=o, S_T=ST, workspace=ws))
+    plain_ms = timed(lambda: binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"],
+                                                   ins["beta"], ins["S0"], o=o, S_T=ST, workspace=ws))
+    del snaps
+    N, Hd, dkd, dvd = d["S"].shape
+    sp = inputs.make_forward(N, draft, Hd, dkd, dvd, "bf16", s0="zero", seed=4321, device=dev)
+    Sck = d["S"].clone()
+    o_sp = torch.empty((N, draft, Hd, dvd), dtype=torch.float32, device=dev)
+    acc = torch.full((N,), accept, dtype=torch.int32, device=dev)
+    Sw = d["S"].clone()
+    ver_ms = timed(lambda: binding.kda_spec_verify(sp["q"], sp["k"], sp["v"], sp["g"], sp["beta"],
+                                                   Sck, o=o_sp))
+    com_ms = timed(lambda: binding.kda_spec_commit(sp["k"], sp["v"], sp["g"], sp["beta"], Sw, acc))
+    o1 = torch.empty((N, Hd, dvd), dtype=torch.float32, device=dev)
+    t0 = {n: sp[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    dec_ms = timed(lambda: binding.kda_decode_step(t0["q"], t0["k"], t0["v"], t0["g"], t0["beta"], Sw,
+                                                   o=o1))
+    state = N * Hd * dkd * dvd * 4
+    tok_in = N * Hd * (3 * dkd + dvd + 1) * 2           # q, k, g, v, beta per draft token
+    ver_bytes = state + draft * (tok_in + N * Hd * dvd * 4)
+    com_bytes = 2 * state + draft * (tok_in - N * Hd * dkd * 2)
+    del sp, Sck, Sw, o_sp
+    return {
+        "snapshots": {"every_tokens": every, "count": T // every,
+                      "bytes": B * (T // every) * H * dk * dv * 4,
+                      "prefill_ms": round(snap_ms, 4), "plain_prefill_ms": round(plain_ms, 4),
+                      "overhead_frac": round(snap_ms / plain_ms - 1.0, 4)},
+        "spec": {"requests": N, "heads": Hd, "draft_tokens": draft, "accepted": accept,
+                 "verify_us": round(ver_ms * 1e3, 2),
+                 "verify_GBps": round(ver_bytes / (ver_ms * 1e-3) / 1e9, 1),
+                 "commit_us": round(com_ms * 1e3, 2),
+                 "commit_GBps": round(com_bytes / (com_ms * 1e-3) / 1e9, 1),
+                 "decode_step_us": round(dec_ms * 1e3, 2),
+                 "verify_plus_commit_vs_decode_steps": round((ver_ms + com_ms) / (draft * dec_ms), 4)},
+    }
 
 
 def cpu_leg(ins, o, ntok, pf):

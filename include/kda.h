@@ -35,6 +35,7 @@
  *    any error nothing is launched and no output is written.
  *  - Log-decays outside [-5, 0] are clamped to the bound; NaN and Inf in any
  *    input propagate to the outputs (there are no device-side error paths).
+ *    With KDA_GATE_SIGMOID, g holds gate logits instead (see kda_gate).
  *  - in_dtype applies to q, k, v, g, beta alike. The state is always fp32.
  */
 #ifndef KDA_H_
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -61,6 +62,20 @@ typedef enum {
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * What the g input holds (the *_ex and kda_spec_* entry points take it; the
+ * others use KDA_GATE_LOG_DECAY).
+ *  KDA_GATE_LOG_DECAY  g is the per-channel log-decay, clamped to [-5, 0].
+ *  KDA_GATE_SIGMOID    g is a raw gate logit x; the log-decay is
+ *                      -5 / (1 + exp(-x)) = -5 sigmoid(x), in (-5, 0): a
+ *                      lower-bounded sigmoid decay whose retention factor
+ *                      never falls below e^-5 ("Kimi K3 goes trillion-scale
+ *                      with sparse MoE efficiency" subtitles, cue 14; the
+ *                      pages give the bound, not the formula: scaling the
+ *                      sigmoid to the bound is this library's reading).
+ */
+typedef enum { KDA_GATE_LOG_DECAY = 0, KDA_GATE_SIGMOID = 1 } kda_gate;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION at build time). */
 int kda_abi_version(void);
@@ -171,6 +186,106 @@ kda_status kda_decode_step_check(const void* q, const void* k, const void* v,
                                  const void* g, const void* beta, const float* S,
                                  const void* o, int64_t N, int64_t H, int64_t dk,
                                  int64_t dv, int in_dtype, int out_dtype);
+
+/*
+ * kda_chunk_fwd with two options.
+ *
+ *   gate            a kda_gate value: how g is read (KDA_ERR_UNSUPPORTED
+ *                   otherwise).
+ *   snapshots,      state snapshots every `snapshot_every` tokens, for prefix
+ *   snapshot_every  reuse: the state after tokens [0, (j+1) * snapshot_every)
+ *                   of sequence b is written to snapshots[b, j] for
+ *                   j = 0 .. T / snapshot_every - 1, with layout
+ *                   [B, T / snapshot_every, H, dk, dv] fp32. snapshot_every
+ *                   is 0 (none; snapshots ignored) or a positive multiple
+ *                   of 16 (KDA_ERR_UNSUPPORTED otherwise; negative is
+ *                   KDA_ERR_SHAPE); snapshots may be NULL only when no
+ *                   snapshot falls inside T. They must not overlap any
+ *                   other tensor or the workspace. 4-byte aligned.
+ *
+ * Snapshots serve a prefix cache that hashes fixed blocks of 512 tokens and
+ * shares the recurrent state of a hit across requests ("177: Kimi K3 in
+ * Detail", sections 10 and 16). Since chunks align at t = 0 and
+ * snapshot_every is a multiple of 16, a later kda_chunk_fwd over the tokens
+ * after snapshot j with S0 = snapshots[b, j] (for B = 1 that block is
+ * exactly an [H, dk, dv] state) performs the same arithmetic as the
+ * uninterrupted run: its o and S_T are bit-identical to the full run's.
+ */
+kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* S0, void* o, float* S_T,
+                            int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                            int in_dtype, int out_dtype, int gate, float* snapshots,
+                            int64_t snapshot_every, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Host-only check of kda_chunk_fwd_ex's arguments (see kda_chunk_fwd_check). */
+kda_status kda_chunk_fwd_ex_check(const void* q, const void* k, const void* v,
+                                  const void* g, const void* beta, const float* S0,
+                                  const void* o, const float* S_T, int64_t B, int64_t T,
+                                  int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                                  int out_dtype, int gate, const float* snapshots,
+                                  int64_t snapshot_every, const void* workspace,
+                                  size_t workspace_bytes);
+
+/* kda_decode_step with a kda_gate value for g (KDA_ERR_UNSUPPORTED otherwise). */
+kda_status kda_decode_step_ex(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, float* S, void* o, int64_t N, int64_t H,
+                              int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                              int gate, void* stream);
+
+/*
+ * Speculative decoding: verification from a checkpoint, then commit by
+ * replay. The state is rewritten by every token, so a rejected draft cannot
+ * be torn off afterwards; instead the state at the last accepted position is
+ * kept, the draft tokens' inputs are logged (about 1 KiB per head and token
+ * at d = 128), and the accepted prefix is replayed from the checkpoint
+ * ("177: Kimi K3 in Detail", section 23; "Kimi K3 goes trillion-scale with
+ * sparse MoE efficiency" subtitles, cue 28).
+ *
+ * kda_spec_verify: for N requests with T draft tokens each, the outputs of
+ * all T tokens, stepping from the checkpoint S, which is only read. o[n, t]
+ * equals what T successive kda_decode_step calls from S would return.
+ *
+ *   q, k, g  [N, T, H, dk]  in_dtype
+ *   v        [N, T, H, dv]  in_dtype
+ *   beta     [N, T, H]      in_dtype
+ *   S        [N, H, dk, dv] fp32, the checkpoint (read only); 16-byte aligned
+ *   o        [N, T, H, dv]  out_dtype; must not overlap any input or S
+ *
+ * kda_spec_commit: S advanced in place over the first accepted[n] tokens of
+ * request n (values outside [0, T] are clamped to it; 0 leaves S unchanged).
+ * The result equals accepted[n] successive kda_decode_step calls. q and o are
+ * not involved.
+ *
+ *   k, g, v, beta   as for kda_spec_verify
+ *   S               [N, H, dk, dv] fp32, in place; 16-byte aligned
+ *   accepted        [N] int32 on the device, 4-byte aligned
+ *
+ * Supported: dk, dv in {64, 128}; N, T, H >= 0; gate a kda_gate value. A
+ * verify + commit pair reads the state twice and writes it once whatever T
+ * is, where T decode steps would read and write it T times each.
+ */
+kda_status kda_spec_verify(const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* S, void* o, int64_t N, int64_t T,
+                           int64_t H, int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                           int gate, void* stream);
+
+kda_status kda_spec_commit(const void* k, const void* v, const void* g, const void* beta,
+                           float* S, const int32_t* accepted, int64_t N, int64_t T,
+                           int64_t H, int64_t dk, int64_t dv, int in_dtype, int gate,
+                           void* stream);
+
+/* Host-only checks of the two calls above (see kda_chunk_fwd_check). */
+kda_status kda_spec_verify_check(const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* S,
+                                 const void* o, int64_t N, int64_t T, int64_t H,
+                                 int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                                 int gate);
+
+kda_status kda_spec_commit_check(const void* k, const void* v, const void* g,
+                                 const void* beta, const float* S,
+                                 const int32_t* accepted, int64_t N, int64_t T, int64_t H,
+                                 int64_t dk, int64_t dv, int in_dtype, int gate);
 
 #ifdef __cplusplus
 }

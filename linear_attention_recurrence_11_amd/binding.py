@@ -14,6 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_GATE_LOG_DECAY, KDA_GATE_SIGMOID = 0, 1
 _STATUS_OK = 0
 
 
@@ -55,6 +56,20 @@ def _load():
         lib.kda_decode_step.argtypes = [vp] * 7 + [i64] * 4 + [i, i, vp]
         lib.kda_decode_step_check.restype = i
         lib.kda_decode_step_check.argtypes = [vp] * 7 + [i64] * 4 + [i, i]
+        lib.kda_chunk_fwd_ex.restype = i
+        lib.kda_chunk_fwd_ex.argtypes = [vp] * 8 + [i64] * 5 + [i, i, i, vp, i64, vp, sz, vp]
+        lib.kda_chunk_fwd_ex_check.restype = i
+        lib.kda_chunk_fwd_ex_check.argtypes = [vp] * 8 + [i64] * 5 + [i, i, i, vp, i64, vp, sz]
+        lib.kda_decode_step_ex.restype = i
+        lib.kda_decode_step_ex.argtypes = [vp] * 7 + [i64] * 4 + [i, i, i, vp]
+        lib.kda_spec_verify.restype = i
+        lib.kda_spec_verify.argtypes = [vp] * 7 + [i64] * 5 + [i, i, i, vp]
+        lib.kda_spec_verify_check.restype = i
+        lib.kda_spec_verify_check.argtypes = [vp] * 7 + [i64] * 5 + [i, i, i]
+        lib.kda_spec_commit.restype = i
+        lib.kda_spec_commit.argtypes = [vp] * 6 + [i64] * 5 + [i, i, vp]
+        lib.kda_spec_commit_check.restype = i
+        lib.kda_spec_commit_check.argtypes = [vp] * 6 + [i64] * 5 + [i, i]
         _LIB = lib
     return _LIB
 
@@ -179,3 +194,84 @@ def kda_decode_step(q, k, v, g, beta, S, *, o=None, out_dtype=torch.float32, str
     if st != _STATUS_OK:
         raise KDAError(st, "kda_decode_step")
     return o
+
+
+def kda_chunk_fwd_ex(q, k, v, g, beta, S0=None, *, gate=KDA_GATE_LOG_DECAY, snapshot_every=0,
+                     snapshots=None, o=None, S_T=None, out_dtype=torch.float32, want_state=True,
+                     workspace=None, stream=None):
+    """kda_chunk_fwd with a gate option (KDA_GATE_SIGMOID: g holds gate logits)
+    and state snapshots every `snapshot_every` tokens (0: none) into
+    `snapshots` [B, T // snapshot_every, H, dk, dv] float32 (allocated here
+    when not given). Returns (o, S_T, snapshots or None)."""
+    lib = _load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dcode(q.dtype)
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    nsnap = T // snapshot_every if snapshot_every > 0 else 0
+    if snapshots is None and nsnap > 0:
+        snapshots = torch.empty((B, nsnap, H, dk, dv), dtype=torch.float32, device=dev)
+    need = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                              _ptr(S_T), B, T, H, dk, dv, code, _dcode(o.dtype), int(gate),
+                              _ptr(snapshots), int(snapshot_every), _ptr(workspace), wbytes,
+                              _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_chunk_fwd_ex")
+    return o, S_T, snapshots
+
+
+def kda_decode_step_ex(q, k, v, g, beta, S, *, gate=KDA_GATE_LOG_DECAY, o=None,
+                       out_dtype=torch.float32, stream=None):
+    """kda_decode_step with a gate option. Returns o [N,H,dv]; S updated in place."""
+    lib = _load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
+    st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                                N, H, dk, dv, _dcode(q.dtype), _dcode(o.dtype), int(gate),
+                                _stream(stream, q.device))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_decode_step_ex")
+    return o
+
+
+def kda_spec_verify(q, k, v, g, beta, S, *, gate=KDA_GATE_LOG_DECAY, o=None,
+                    out_dtype=torch.float32, stream=None):
+    """Outputs of T draft tokens per request from the checkpoint S (read only).
+    q, k, g [N,T,H,dk]; v [N,T,H,dv]; beta [N,T,H]; S [N,H,dk,dv] float32.
+    Returns o [N,T,H,dv]."""
+    lib = _load()
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, T, H, dv), dtype=out_dtype, device=q.device)
+    st = lib.kda_spec_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                             N, T, H, dk, dv, _dcode(q.dtype), _dcode(o.dtype), int(gate),
+                             _stream(stream, q.device))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_spec_verify")
+    return o
+
+
+def kda_spec_commit(k, v, g, beta, S, accepted, *, gate=KDA_GATE_LOG_DECAY, stream=None):
+    """Advance the checkpoint S [N,H,dk,dv] in place over the first accepted[n]
+    (int32 [N] on the device) of the T logged tokens. Returns S."""
+    lib = _load()
+    N, T, H, dk = k.shape
+    dv = v.shape[-1]
+    if accepted.dtype != torch.int32:
+        raise TypeError("accepted must be int32")
+    st = lib.kda_spec_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(accepted),
+                             N, T, H, dk, dv, _dcode(k.dtype), int(gate), _stream(stream, k.device))
+    if st != _STATUS_OK:
+        raise KDAError(st, "kda_spec_commit")
+    return S

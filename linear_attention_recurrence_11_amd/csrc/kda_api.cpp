@@ -72,6 +72,8 @@ struct ChunkPtrs {
   const float* S_T;
   const void* ws;
   size_t ws_bytes;
+  const float* snaps = nullptr;  // state snapshots (pass stage), or NULL
+  int64_t snap_every = 0;
 };
 
 // The argument rules of include/kda.h for the tensors a stage touches:
@@ -125,8 +127,22 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
   }
   if (overlap(ro, rst) || overlap(ro, rw) || overlap(rw, rst)) return KDA_ERR_ALIAS;
   if (overlap(rst, rs0) && p.S_T != p.S0) return KDA_ERR_ALIAS;
+  // snapshots: [B, T / every, H, dk, dv] fp32 written by the pass stage
+  if (p.snap_every < 0) return KDA_ERR_SHAPE;
+  if (p.snap_every % 16 != 0) return KDA_ERR_UNSUPPORTED;
+  const int64_t nsnap = p.snap_every > 0 ? T / p.snap_every : 0;
+  if (pass && nsnap > 0) {
+    if (!p.snaps) return KDA_ERR_NULL;
+    if (!aligned(p.snaps, 4)) return KDA_ERR_ALIGNMENT;
+    const Range rsn = range_of(p.snaps, B * nsnap * H * dk * dv, 4);
+    const Range all[] = {rq, rk, rv, rg, rb, rs0, ro, rst, rw};
+    for (const Range& x : all)
+      if (overlap(rsn, x)) return KDA_ERR_ALIAS;
+  }
   return KDA_OK;
 }
+
+bool gate_ok(int gate) { return gate == KDA_GATE_LOG_DECAY || gate == KDA_GATE_SIGMOID; }
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
@@ -152,6 +168,36 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
   if (st != KDA_OK) return st;
   if (B * H == 0) return KDA_OK;
   kda::ChunkFwdArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype, workspace};
+  return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_chunk_fwd_ex_check(const void* q, const void* k, const void* v, const void* g,
+                                  const void* beta, const float* S0, const void* o,
+                                  const float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                  int64_t dv, int in_dtype, int out_dtype, int gate,
+                                  const float* snapshots, int64_t snapshot_every,
+                                  const void* workspace, size_t workspace_bytes) {
+  if (!gate_ok(gate)) return KDA_ERR_UNSUPPORTED;
+  ChunkPtrs p{q, k, v, g, beta, S0, o, S_T, workspace, workspace_bytes};
+  p.snaps = snapshots;
+  p.snap_every = snapshot_every;
+  return check_chunk(p, B, T, H, dk, dv, in_dtype, out_dtype, kPrep | kPass);
+}
+
+kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* S0, void* o, float* S_T, int64_t B,
+                            int64_t T, int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                            int out_dtype, int gate, float* snapshots, int64_t snapshot_every,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const kda_status st =
+      kda_chunk_fwd_ex_check(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype,
+                             gate, snapshots, snapshot_every, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  if (B * H == 0) return KDA_OK;
+  kda::ChunkFwdArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype, workspace};
+  a.gate = gate;
+  a.snapshots = snapshots;
+  a.snapshot_every = snapshot_every;
   return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -211,13 +257,104 @@ kda_status kda_decode_step_check(const void* q, const void* k, const void* v, co
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                            const void* beta, float* S, void* o, int64_t N, int64_t H, int64_t dk,
                            int64_t dv, int in_dtype, int out_dtype, void* stream) {
+  return kda_decode_step_ex(q, k, v, g, beta, S, o, N, H, dk, dv, in_dtype, out_dtype,
+                            KDA_GATE_LOG_DECAY, stream);
+}
+
+kda_status kda_decode_step_ex(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, float* S, void* o, int64_t N, int64_t H,
+                              int64_t dk, int64_t dv, int in_dtype, int out_dtype, int gate,
+                              void* stream) {
+  if (!gate_ok(gate)) return KDA_ERR_UNSUPPORTED;
   const kda_status st =
       kda_decode_step_check(q, k, v, g, beta, S, o, N, H, dk, dv, in_dtype, out_dtype);
   if (st != KDA_OK) return st;
   if (N * H == 0) return KDA_OK;
   kda::DecodeArgs a{q, k, v, g, beta, S, o, N, H, dk, dv, in_dtype, out_dtype};
-  const hipError_t e = kda::launch_decode_step(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  a.gate = gate;
+  return launch_status(kda::launch_decode_step(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Arguments of kda_spec_verify (commit = false) and kda_spec_commit (true).
+kda_status check_spec(bool commit, const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, const float* S, const void* o, const int32_t* accepted,
+                      int64_t N, int64_t T, int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                      int out_dtype, int gate) {
+  if (N < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return KDA_ERR_SHAPE;
+  if (!dtype_ok(in_dtype) || (!commit && !dtype_ok(out_dtype)) || !gate_ok(gate))
+    return KDA_ERR_UNSUPPORTED;
+  if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
+  if (N > 0x7fffffffLL || H > 0x7fffffffLL || N * H > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
+  if (T > kMaxElems || static_cast<double>(N) * H * T * 128 > static_cast<double>(kMaxElems))
+    return KDA_ERR_SHAPE;
+  const int64_t NH = N * H, NTH = N * T * H;
+  if (NH == 0 || T == 0) return KDA_OK;
+  if (!k || !v || !g || !beta || !S) return KDA_ERR_NULL;
+  if (commit ? !accepted : (!q || !o)) return KDA_ERR_NULL;
+  const int64_t es = dsize(in_dtype), eo = dsize(out_dtype);
+  const void* elem[] = {commit ? k : q, k, v, g, beta};
+  for (const void* p : elem)
+    if (!aligned(p, es)) return KDA_ERR_ALIGNMENT;
+  if (!aligned(S, 16)) return KDA_ERR_ALIGNMENT;
+  if (commit ? !aligned(accepted, 4) : !aligned(o, eo)) return KDA_ERR_ALIGNMENT;
+  const Range none{0, 0};
+  const Range rs = range_of(S, NH * dk * dv, 4);
+  const Range rout = commit ? rs : range_of(o, NTH * dv, eo);  // what the call writes
+  const Range ins[] = {commit ? none : range_of(q, NTH * dk, es), range_of(k, NTH * dk, es),
+                       range_of(v, NTH * dv, es), range_of(g, NTH * dk, es),
+                       range_of(beta, NTH, es), commit ? range_of(accepted, N, 4) : rs};
+  for (const Range& x : ins)
+    if (overlap(rout, x)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_spec_verify_check(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const float* S, const void* o, int64_t N,
+                                 int64_t T, int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                                 int out_dtype, int gate) {
+  return check_spec(false, q, k, v, g, beta, S, o, nullptr, N, T, H, dk, dv, in_dtype, out_dtype,
+                    gate);
+}
+
+kda_status kda_spec_verify(const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* S, void* o, int64_t N, int64_t T,
+                           int64_t H, int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                           int gate, void* stream) {
+  const kda_status st =
+      kda_spec_verify_check(q, k, v, g, beta, S, o, N, T, H, dk, dv, in_dtype, out_dtype, gate);
+  if (st != KDA_OK) return st;
+  if (N * H == 0 || T == 0) return KDA_OK;
+  kda::SpecArgs a{q, k, v, g, beta, const_cast<float*>(S), o, nullptr, N, T, H, dk, dv,
+                  in_dtype, out_dtype};
+  a.gate = gate;
+  return launch_status(kda::launch_spec(a, false, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_spec_commit_check(const void* k, const void* v, const void* g, const void* beta,
+                                 const float* S, const int32_t* accepted, int64_t N, int64_t T,
+                                 int64_t H, int64_t dk, int64_t dv, int in_dtype, int gate) {
+  return check_spec(true, nullptr, k, v, g, beta, S, nullptr, accepted, N, T, H, dk, dv, in_dtype,
+                    KDA_F32, gate);
+}
+
+kda_status kda_spec_commit(const void* k, const void* v, const void* g, const void* beta,
+                           float* S, const int32_t* accepted, int64_t N, int64_t T, int64_t H,
+                           int64_t dk, int64_t dv, int in_dtype, int gate, void* stream) {
+  const kda_status st =
+      kda_spec_commit_check(k, v, g, beta, S, accepted, N, T, H, dk, dv, in_dtype, gate);
+  if (st != KDA_OK) return st;
+  if (N * H == 0 || T == 0) return KDA_OK;
+  kda::SpecArgs a{nullptr, k, v, g, beta, S, nullptr, accepted, N, T, H, dk, dv, in_dtype, KDA_F32};
+  a.gate = gate;
+  return launch_status(kda::launch_spec(a, true, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -18,7 +18,7 @@
 namespace kda {
 namespace {
 
-template <typename InT, typename OutT, int DK, int DV>
+template <typename InT, typename OutT, int DK, int DV, int GATE>
 __global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__ q,
                                                          const InT* __restrict__ k,
                                                          const InT* __restrict__ v,
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__
   for (int i = t; i < DK; i += 256) {
     s_q[i] = load_in(q, unit * DK + i);
     s_k[i] = load_in(k, unit * DK + i);
-    s_e[i] = expf(clamp_decay(load_in(g, unit * DK + i)));
+    s_e[i] = expf(gate_decay<GATE>(load_in(g, unit * DK + i)));
   }
   __syncthreads();
   if (t < 64) {  // q . k by one wavefront
@@ -105,15 +105,21 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__
   }
 }
 
-template <typename InT, typename OutT, int DK, int DV>
-hipError_t launch4(const DecodeArgs& a, hipStream_t stream) {
+template <typename InT, typename OutT, int DK, int DV, int GATE>
+hipError_t launch5(const DecodeArgs& a, hipStream_t stream) {
   const int64_t units = a.N * a.H;
-  hipLaunchKernelGGL((kda_decode_kernel<InT, OutT, DK, DV>), dim3(static_cast<uint32_t>(units)),
+  hipLaunchKernelGGL((kda_decode_kernel<InT, OutT, DK, DV, GATE>), dim3(static_cast<uint32_t>(units)),
                      dim3(256), 0, stream, static_cast<const InT*>(a.q),
                      static_cast<const InT*>(a.k), static_cast<const InT*>(a.v),
                      static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta), a.S,
                      static_cast<OutT*>(a.o));
   return hipGetLastError();
+}
+
+template <typename InT, typename OutT, int DK, int DV>
+hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
+  return a.gate == kGateSigmoid ? launch5<InT, OutT, DK, DV, kGateSigmoid>(a, s)
+                                : launch5<InT, OutT, DK, DV, kGateLogDecay>(a, s);
 }
 
 template <typename InT, typename OutT>

@@ -59,6 +59,21 @@ __device__ __forceinline__ float clamp_decay(float x) {
   return x < -5.0f ? -5.0f : (x > 0.0f ? 0.0f : x);
 }
 
+// Per-channel log-decay from the g input. GATE 0: g is the log-decay itself
+// (floored at -5, capped at 0). GATE 1: g is a raw gate logit x and the
+// log-decay is the sigmoid scaled to the floor, -5 / (1 + e^-x), a lower-
+// bounded sigmoid decay whose retention never drops below e^-5 ("Kimi K3
+// goes trillion-scale with sparse MoE efficiency" subtitles, cue 14; "K3 tech
+// report" podcast, the decay-bound exchange). The clamp then only passes NaN.
+template <int GATE>
+__device__ __forceinline__ float gate_decay(float x) {
+  if constexpr (GATE == 1) {
+    return clamp_decay(-5.0f / (1.0f + __expf(-x)));
+  } else {
+    return clamp_decay(x);
+  }
+}
+
 // ---- DPP row scans (a row is 16 consecutive lanes) -----------------------
 
 template <int kCtrl>

@@ -35,6 +35,9 @@ inline RecordLayout record_layout(int64_t dk, bool f32_path) {
   return L;
 }
 
+// How the g input becomes the per-channel log-decay (kda_gate values).
+enum GateMode : int { kGateLogDecay = 0, kGateSigmoid = 1 };
+
 struct ChunkFwdArgs {
   const void *q, *k, *v, *g, *beta;
   const float* S0;
@@ -43,6 +46,9 @@ struct ChunkFwdArgs {
   int64_t B, T, H, dk, dv;
   int in_dtype, out_dtype;  // kda_dtype values
   void* workspace;
+  int gate = kGateLogDecay;
+  float* snapshots = nullptr;     // [B, T / snapshot_every, H, dk, dv] or null
+  int64_t snapshot_every = 0;     // tokens between snapshots, a multiple of 16
 };
 
 struct DecodeArgs {
@@ -51,6 +57,20 @@ struct DecodeArgs {
   void* o;
   int64_t N, H, dk, dv;
   int in_dtype, out_dtype;
+  int gate = kGateLogDecay;
+};
+
+// Speculative verification / commit over T logged tokens per request.
+// verify: o for all T tokens from S, S unchanged; commit: S advanced in place
+// by accepted[n] tokens (clamped to [0, T]), no output.
+struct SpecArgs {
+  const void *q, *k, *v, *g, *beta;
+  float* S;
+  void* o;
+  const int32_t* accepted;
+  int64_t N, T, H, dk, dv;
+  int in_dtype, out_dtype;
+  int gate = kGateLogDecay;
 };
 
 // Launch the chunkwise forward (prep kernel then state pass) on `stream`.
@@ -61,5 +81,8 @@ hipError_t launch_chunk_state_pass(const ChunkFwdArgs& a, hipStream_t stream);
 
 // Launch one decode step on `stream`.
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
+
+// Launch a speculative verification (commit = false) or commit (commit = true).
+hipError_t launch_spec(const SpecArgs& a, bool commit, hipStream_t stream);
 
 }  // namespace kda

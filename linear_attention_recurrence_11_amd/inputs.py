@@ -16,6 +16,9 @@ Recipe (per workload, one torch generator seeded with the workload seed):
     g     = max(-5, -softplus(N(0,1))) per channel; with a pinned fraction p,
             a seeded random p*dk channels of every head are -5 at every token
     S0    = 0, or 0.02 * N(0,1) in fp32
+    gate logits (for the sigmoid-gate option, replacing g): 2 * N(0,1) - 2,
+            so the log-decay -5 sigmoid(x) averages about -1 with a spread
+            over most of (-5, 0)
 Layouts: q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; S0 [B,H,dk,dv].
 Decode steps: q, k, g [steps,N,H,dk]; v [steps,N,H,dv]; beta [steps,N,H];
 state S [N,H,dk,dv] fp32.
@@ -52,6 +55,10 @@ def _decay(x):
     return torch.clamp(-torch.nn.functional.softplus(x), min=-5.0)
 
 
+def _logit(x):
+    return 2.0 * x - 2.0
+
+
 def make_generator(seed, device):
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
@@ -59,14 +66,16 @@ def make_generator(seed, device):
 
 
 def make_forward(B, T, H, dk, dv, in_dtype="bf16", s0="zero", pinned_fraction=0.0,
-                 seed=0, device="cpu"):
+                 seed=0, device="cpu", gate_logits=False):
+    """Forward inputs; with gate_logits=True, g holds gate logits (recipe above)
+    instead of log-decays."""
     dt = _dt(in_dtype)
     gen = make_generator(seed, device)
     q = _blocked(gen, B, T, H, dk, device, _unit, dt)
     k = _blocked(gen, B, T, H, dk, device, _unit, dt)
     v = _blocked(gen, B, T, H, dv, device, lambda x: x, dt)
     beta = _blocked(gen, B, T, H, None, device, torch.sigmoid, dt)
-    g = _blocked(gen, B, T, H, dk, device, _decay, dt)
+    g = _blocked(gen, B, T, H, dk, device, _logit if gate_logits else _decay, dt)
     if s0 == "zero":
         S0 = None
     else:
@@ -84,7 +93,7 @@ def make_forward(B, T, H, dk, dv, in_dtype="bf16", s0="zero", pinned_fraction=0.
     return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
 
 
-def make_decode(N, steps, H, dk, dv, in_dtype="bf16", seed=0, device="cpu"):
+def make_decode(N, steps, H, dk, dv, in_dtype="bf16", seed=0, device="cpu", gate_logits=False):
     dt = _dt(in_dtype)
     gen = make_generator(seed, device)
     S = 0.02 * _normal(gen, (N, H, dk, dv), device)
@@ -92,7 +101,7 @@ def make_decode(N, steps, H, dk, dv, in_dtype="bf16", seed=0, device="cpu"):
     k = _unit(_normal(gen, (steps, N, H, dk), device)).to(dt)
     v = _normal(gen, (steps, N, H, dv), device).to(dt)
     beta = torch.sigmoid(_normal(gen, (steps, N, H), device)).to(dt)
-    g = _decay(_normal(gen, (steps, N, H, dk), device)).to(dt)
+    g = (_logit if gate_logits else _decay)(_normal(gen, (steps, N, H, dk), device)).to(dt)
     return dict(S=S, q=q, k=k, v=v, g=g, beta=beta)
 
 

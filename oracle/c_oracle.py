@@ -13,6 +13,7 @@ from . import build as _build
 
 _lib = None
 F32, BF16 = 0, 1
+GATE_LOG_DECAY, GATE_SIGMOID = 0, 1
 
 
 def _load():
@@ -23,9 +24,9 @@ def _load():
             _build.build()
         lib = ctypes.CDLL(path)
         vp, l, i = ctypes.c_void_p, ctypes.c_long, ctypes.c_int
-        lib.kda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, l, l, l, l, l, i]
+        lib.kda_oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, vp, vp, vp, l, l, l, l, l, i]
         lib.kda_oracle_fwd.restype = i
-        lib.kda_oracle_fwd_cols.argtypes = [vp, vp, vp, vp, vp, i, l, l, l, l, l, l, l,
+        lib.kda_oracle_fwd_cols.argtypes = [vp, vp, vp, vp, vp, i, i, l, l, l, l, l, l, l,
                                             vp, l, vp, vp, vp]
         lib.kda_oracle_fwd_cols.restype = i
         _lib = lib
@@ -52,9 +53,10 @@ def default_threads():
         return os.cpu_count() or 1
 
 
-def fwd(q, k, v, g, beta, S0=None, nthreads=None, want_o=True, want_state=True):
+def fwd(q, k, v, g, beta, S0=None, nthreads=None, want_o=True, want_state=True, gate=GATE_LOG_DECAY):
     """Sequential fp64 recurrence. Shapes: q,k,g [B,T,H,dk]; v [B,T,H,dv];
     beta [B,T,H]; S0 [B,H,dk,dv] (any float dtype, widened to double) or None.
+    gate=GATE_SIGMOID reads g as gate logits x with log-decay -5 sigmoid(x).
     Returns (o [B,T,H,dv] float64 or None, S_T [B,H,dk,dv] float64 or None)."""
     q, k, v, g, beta = (np.ascontiguousarray(x) for x in (q, k, v, g, beta))
     code = _dtype_code([q, k, v, g, beta])
@@ -68,7 +70,7 @@ def fwd(q, k, v, g, beta, S0=None, nthreads=None, want_o=True, want_state=True):
         assert s0.shape == (B, H, dk, dv)
     o = np.empty((B, T, H, dv), np.float64) if want_o else None
     st = np.empty((B, H, dk, dv), np.float64) if want_state else None
-    rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), code,
+    rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), code, int(gate),
                                 _ptr(s0), _ptr(o), _ptr(st), B, T, H, dk, dv,
                                 int(nthreads or default_threads()))
     if rc != 0:
@@ -76,7 +78,7 @@ def fwd(q, k, v, g, beta, S0=None, nthreads=None, want_o=True, want_state=True):
     return o, st
 
 
-def fwd_cols(q, k, v, g, beta, b, h, cols, S0c=None):
+def fwd_cols(q, k, v, g, beta, b, h, cols, S0c=None, gate=GATE_LOG_DECAY):
     """The recurrence for one (b, h) restricted to value columns `cols`.
     Returns (o_cols [T, ncols], S_T cols [dk, ncols]) in float64."""
     q, k, v, g, beta = (np.ascontiguousarray(x) for x in (q, k, v, g, beta))
@@ -91,7 +93,7 @@ def fwd_cols(q, k, v, g, beta, b, h, cols, S0c=None):
     oc = np.empty((T, n), np.float64)
     stc = np.empty((dk, n), np.float64)
     rc = _load().kda_oracle_fwd_cols(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), code,
-                                     B, T, H, dk, dv, int(b), int(h), _ptr(cols), n,
+                                     int(gate), B, T, H, dk, dv, int(b), int(h), _ptr(cols), n,
                                      _ptr(s0), _ptr(oc), _ptr(stc))
     if rc != 0:
         raise ValueError("kda_oracle_fwd_cols rejected its arguments (code %d)" % rc)

@@ -27,6 +27,12 @@
  * in double precision. NaN in any input propagates (the clamp compares, it does
  * not use fmin/fmax).
  *
+ * Gate option (gate = 1): g holds raw gate logits x instead of log-decays, and
+ * the log-decay is -5 sigmoid(x) = -5 / (1 + exp(-x)) before the clamp (which
+ * then only passes NaN). The pages state the bound (retention floored at
+ * e^-5, a "lower-bounded sigmoid" decay) but not the formula; a sigmoid
+ * scaled to the bound is the reading taken (same subtitle cue 14).
+ *
  * Inputs may be fp32 or bf16 bit patterns; they are widened to double exactly.
  * Layout: q, k, g are [B, T, H, dk]; v is [B, T, H, dv]; beta is [B, T, H];
  * S0 and S_T are [B, H, dk, dv] (double); o is [B, T, H, dv] (double).
@@ -39,6 +45,8 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_GATE_LOG_DECAY 0
+#define ORACLE_GATE_SIGMOID 1
 
 static double widen(const void* base, int dtype, size_t idx) {
     if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
@@ -54,9 +62,15 @@ static double clamp_decay(double x) {
     return x;
 }
 
+/* Per-channel log-decay of one g entry under the gate option. */
+static double log_decay(double x, int gate) {
+    if (gate == ORACLE_GATE_SIGMOID) x = -5.0 / (1.0 + exp(-x));
+    return clamp_decay(x);
+}
+
 typedef struct {
     const void *q, *k, *v, *g, *beta;
-    int dtype;
+    int dtype, gate;
     const double* S0;  /* [B,H,dk,dv] or NULL */
     double* o;         /* [B,T,H,dv] or NULL */
     double* ST;        /* [B,H,dk,dv] or NULL */
@@ -75,7 +89,7 @@ static void run_unit(fwd_job* J, long unit, double* S, double* gq, double* gk,
     for (long t = 0; t < T; ++t) {
         const size_t tok = (size_t)(b * T + t) * H + h;
         for (long i = 0; i < dk; ++i) {
-            e[i] = exp(clamp_decay(widen(J->g, J->dtype, tok * dk + i)));
+            e[i] = exp(log_decay(widen(J->g, J->dtype, tok * dk + i), J->gate));
             gk[i] = widen(J->k, J->dtype, tok * dk + i);
             gq[i] = widen(J->q, J->dtype, tok * dk + i);
         }
@@ -124,15 +138,16 @@ static void* worker(void* arg) {
 
 /* Full forward. Returns 0 on success, nonzero on bad arguments. */
 int kda_oracle_fwd(const void* q, const void* k, const void* v, const void* g,
-                   const void* beta, int dtype, const double* S0, double* o,
+                   const void* beta, int dtype, int gate, const double* S0, double* o,
                    double* ST, long B, long T, long H, long dk, long dv,
                    int nthreads) {
     if (!q || !k || !v || !g || !beta) return 1;
     if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1) return 2;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
+    if (gate != ORACLE_GATE_LOG_DECAY && gate != ORACLE_GATE_SIGMOID) return 3;
     fwd_job J;
     memset(&J, 0, sizeof J);
-    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.dtype = dtype;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.dtype = dtype; J.gate = gate;
     J.S0 = S0; J.o = o; J.ST = ST;
     J.B = B; J.T = T; J.H = H; J.dk = dk; J.dv = dv; J.next_unit = 0;
     pthread_mutex_init(&J.lock, NULL);
@@ -156,11 +171,12 @@ int kda_oracle_fwd(const void* q, const void* k, const void* v, const void* g,
  * [T, ncols]; STc is [dk, ncols] (either may be NULL).
  */
 int kda_oracle_fwd_cols(const void* q, const void* k, const void* v, const void* g,
-                        const void* beta, int dtype, long B, long T, long H,
+                        const void* beta, int dtype, int gate, long B, long T, long H,
                         long dk, long dv, long b, long h, const long* cols,
                         long ncols, const double* S0c, double* oc, double* STc) {
     if (!q || !k || !v || !g || !beta || !cols) return 1;
     if (b < 0 || b >= B || h < 0 || h >= H || ncols < 1) return 2;
+    if (gate != ORACLE_GATE_LOG_DECAY && gate != ORACLE_GATE_SIGMOID) return 3;
     for (long c = 0; c < ncols; ++c)
         if (cols[c] < 0 || cols[c] >= dv) return 2;
     double* S = (double*)calloc((size_t)dk * ncols, sizeof(double));
@@ -171,7 +187,7 @@ int kda_oracle_fwd_cols(const void* q, const void* k, const void* v, const void*
     for (long t = 0; t < T; ++t) {
         const size_t tok = (size_t)(b * T + t) * H + h;
         for (long i = 0; i < dk; ++i) {
-            e[i] = exp(clamp_decay(widen(g, dtype, tok * dk + i)));
+            e[i] = exp(log_decay(widen(g, dtype, tok * dk + i), gate));
             gk[i] = widen(k, dtype, tok * dk + i);
             gq[i] = widen(q, dtype, tok * dk + i);
         }

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.kda_abi_version() == 1
+    assert binding.kda_abi_version() == 2
     for s in range(8):
         assert binding.kda_status_str(s) and binding.kda_status_str(s) != "unknown status"
     assert binding.kda_status_str(99) == "unknown status"
@@ -191,3 +191,78 @@ def test_stage_entry_points_check_their_own_tensors(lib):
     assert passf(S_T=p["S0"] + 128) == ALIAS
     assert passf(v=p["v"] + 2) == ALIGN
     assert passf(v=p["v"] + 8) == ALIGN      # v: 16 bytes
+
+
+def check_ex(lib, p, sizes, gate=0, snaps=None, every=0, **over):
+    p = dict(p)
+    p.update(over)
+    B, T, H, dk, dv, ind, outd = sizes
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    return lib.kda_chunk_fwd_ex_check(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]), vp(p["beta"]),
+                                      vp(p["S0"]), vp(p["o"]), vp(p["S_T"]), B, T, H, dk, dv, ind,
+                                      outd, gate, vp(snaps), every, vp(p["ws"]), p["ws_bytes"])
+
+
+def test_chunk_ex_check_gate_and_snapshots(lib):
+    p, sz = fake_chunk(T=1040)           # 1040 = 2 * 512 + 16: two snapshots at every = 512
+    snaps = BASE + (1 << 36)             # far from every other fake tensor
+    assert check_ex(lib, p, sz) == OK
+    assert check_ex(lib, p, sz, gate=1) == OK
+    assert check_ex(lib, p, sz, gate=2) == UNSUP
+    assert check_ex(lib, p, sz, snaps=snaps, every=512) == OK
+    assert check_ex(lib, p, sz, snaps=snaps, every=16) == OK
+    assert check_ex(lib, p, sz, snaps=None, every=512) == NULL
+    assert check_ex(lib, p, sz, snaps=None, every=2048) == OK      # none falls inside T
+    assert check_ex(lib, p, sz, snaps=snaps, every=-16) == SHAPE
+    assert check_ex(lib, p, sz, snaps=snaps, every=500) == UNSUP
+    assert check_ex(lib, p, sz, snaps=snaps + 2, every=512) == ALIGN
+    assert check_ex(lib, p, sz, snaps=p["o"], every=512) == ALIAS
+    assert check_ex(lib, p, sz, snaps=p["S0"], every=512) == ALIAS
+    assert check_ex(lib, p, sz, snaps=p["ws"], every=512) == ALIAS
+    # the plain checks still apply
+    assert check_ex(lib, p, sz, o=p["q"]) == ALIAS
+    vp = ctypes.c_void_p
+    B, T, H, dk, dv, ind, outd = sz
+    st = lib.kda_chunk_fwd_ex(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]), vp(p["beta"]),
+                              vp(p["S0"]), vp(p["o"]), vp(p["S_T"]), B, T, H, dk, dv, ind, outd,
+                              3, None, 0, vp(p["ws"]), p["ws_bytes"], None)
+    assert st == UNSUP
+
+
+def test_decode_ex_rejects_unknown_gate(lib):
+    vp = ctypes.c_void_p
+    a = [BASE + i * (1 << 24) for i in range(7)]
+    st = lib.kda_decode_step_ex(*[vp(x) for x in a], 4, 2, 128, 128, BF16, F32, 5, None)
+    assert st == UNSUP
+    st = lib.kda_decode_step_ex(*[vp(x) for x in a[:6]], vp(a[5]), 4, 2, 128, 128, BF16, F32, 1,
+                                None)
+    assert st == ALIAS
+
+
+def test_spec_checks(lib):
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    N, T, H, dk, dv = 3, 4, 2, 128, 64
+    a = [BASE + i * (1 << 24) for i in range(8)]   # q k v g beta S o accepted
+    ver = lambda ptrs, T=T, dv=dv, gate=0: lib.kda_spec_verify_check(
+        *[vp(x) for x in ptrs[:7]], N, T, H, dk, dv, BF16, F32, gate)
+    com = lambda ptrs, T=T, gate=0: lib.kda_spec_commit_check(
+        *[vp(x) for x in ptrs[1:6] + [ptrs[7]]], N, T, H, dk, dv, BF16, gate)
+    assert ver(a) == OK and com(a) == OK
+    assert ver(a, gate=1) == OK and com(a, gate=1) == OK
+    assert ver(a, gate=2) == UNSUP and com(a, gate=9) == UNSUP
+    assert ver(a, dv=96) == UNSUP
+    assert ver([None] + a[1:]) == NULL                        # verify reads q
+    assert com([None] + a[1:]) == OK                          # commit does not
+    assert com(a[:7] + [None]) == NULL                        # commit needs accepted
+    assert ver(a[:6] + [a[5]] + a[7:]) == ALIAS               # o over the checkpoint
+    assert ver(a[:6] + [a[1]] + a[7:]) == ALIAS               # o over k
+    assert com(a[:5] + [a[2]] + a[6:]) == ALIAS               # S over v
+    assert com(a[:7] + [a[5]]) == ALIAS                       # accepted over S
+    assert ver(a[:5] + [a[5] + 8] + a[6:]) == ALIGN           # state: 16 bytes
+    assert com(a[:7] + [a[7] + 2]) == ALIGN                   # accepted: 4 bytes
+    assert ver([None] * 8, T=0) == OK and com([None] * 8, T=0) == OK
+    st = lib.kda_spec_verify(*[vp(x) for x in a[:6]], vp(a[5]), N, T, H, dk, dv, BF16, F32, 0, None)
+    assert st == ALIAS
+    st = lib.kda_spec_commit(*[vp(x) for x in a[1:5]], vp(a[5]), vp(a[5]), N, T, H, dk, dv, BF16, 0,
+                             None)
+    assert st == ALIAS

@@ -1,0 +1,261 @@
+"""GPU parity of the options built on the hot path, through the C ABI:
+
+- state snapshots every `snapshot_every` tokens in the chunk forward, and
+  resuming from one (prefix reuse: "177: Kimi K3 in Detail", sections 10, 16);
+- speculative verification from a checkpoint and commit by replay (same page,
+  section 23);
+- the sigmoid gate option (g read as gate logits, log-decay -5 sigmoid(x)).
+
+Expected values come from the fp64 oracle on the same seeded inputs (snapshot
+j = the oracle's final state over the first (j+1)*every tokens; verify = the
+oracle's outputs over the draft tokens from the checkpoint; commit = the
+oracle's state over the accepted prefix), with the bars of the forward:
+max |x - ref| / rms(ref) <= 2e-2 for bf16 inputs, 1e-4 for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpucase import TOL, announce, head_slice, oracle_columns, oracle_forward, rel_err
+from linear_attention_recurrence_11_amd import binding, configs, inputs
+from oracle import c_oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SIG = binding.KDA_GATE_SIGMOID
+
+
+def _prefix(ins, t1):
+    # views: the oracle helpers copy what they need to the host
+    out = {n: ins[n][:, :t1] for n in ("q", "k", "v", "g", "beta")}
+    out["S0"] = ins["S0"]
+    return out
+
+
+def _suffix(ins, t0, S0):
+    out = {n: ins[n][:, t0:].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    out["S0"] = S0
+    return out
+
+
+def _oracle(ins, gate=0):
+    to = inputs.to_oracle
+    S0 = None if ins["S0"] is None else ins["S0"].detach().cpu().numpy()
+    return c_oracle.fwd(to(ins["q"]), to(ins["k"]), to(ins["v"]), to(ins["g"]), to(ins["beta"]),
+                        S0, gate=gate)
+
+
+# ---------------------------------------------------------------- snapshots
+
+@pytest.mark.parametrize("dt,T,every", [("bf16", 1100, 512), ("f32", 200, 16), ("bf16", 1024, 256)])
+def test_snapshots_match_oracle_prefix_states(dt, T, every):
+    announce("snapshots", dt, "T", T, "every", every)
+    ins = inputs.make_forward(2, T, 3, 128, 64, dt, s0="normal", seed=T + every, device=DEV)
+    o, ST, snaps = binding.kda_chunk_fwd_ex(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                            ins["S0"], snapshot_every=every)
+    torch.cuda.synchronize()
+    ns = T // every
+    assert snaps.shape == (2, ns, 3, 128, 64)
+    # the snapshots change nothing else: same o and S_T as the plain forward
+    o2, ST2 = binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(ST, ST2)
+    for j in sorted({0, ns // 2, ns - 1}):
+        _, S_ref = _oracle(_prefix(ins, (j + 1) * every))
+        e = rel_err(snaps[:, j].cpu().numpy(), S_ref)
+        announce("snapshot", j, "err %.3g" % e)
+        assert e <= TOL[dt]
+
+
+def test_resume_from_snapshot_is_bit_identical():
+    # Chunks align at t = 0 and snapshots fall on chunk boundaries, so resuming
+    # from snapshot j performs exactly the arithmetic of the uninterrupted run.
+    T, every = 2048 + 37, 512
+    announce("resume", "T", T, "every", every)
+    ins = inputs.make_forward(1, T, 4, 128, 128, "bf16", s0="normal", seed=99, device=DEV)
+    o, ST, snaps = binding.kda_chunk_fwd_ex(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                            ins["S0"], snapshot_every=every)
+    torch.cuda.synchronize()
+    for j in (0, 2, 3):
+        t0 = (j + 1) * every
+        r = _suffix(ins, t0, snaps[0, j][None].contiguous())
+        o_r, ST_r = binding.kda_chunk_fwd(r["q"], r["k"], r["v"], r["g"], r["beta"], r["S0"])
+        torch.cuda.synchronize()
+        assert torch.equal(o_r, o[:, t0:]), j
+        assert torch.equal(ST_r, ST), j
+
+
+def test_snapshots_at_full_prefill_size_sampled():
+    w = configs.PREFILL_64K
+    every = 512
+    announce("workload", w.name, "snapshots every", every)
+    ins = inputs.make_workload(w, device=DEV)
+    o, ST, snaps = binding.kda_chunk_fwd_ex(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                            ins["S0"], snapshot_every=every)
+    torch.cuda.synchronize()
+    assert snaps.shape == (1, w.T // every, w.H, w.dk, w.dv)
+    cols = [0, 37, 64, 127]
+    for h, j in ((0, 0), (5, 63), (31, 127)):
+        t1 = (j + 1) * every
+        pre = _prefix(ins, t1)
+        _, S_cols = oracle_columns(pre, 0, h, cols)
+        e = rel_err(snaps[0, j, h][:, cols].cpu().numpy(), S_cols)
+        announce("head", h, "snapshot", j, "err %.3g" % e)
+        assert e <= TOL["bf16"]
+    del ins, o, ST, snaps
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------- speculative decoding
+
+def _spec_inputs(N, T, H, dk, dv, dt, seed, gate_logits=False):
+    return inputs.make_forward(N, T, H, dk, dv, dt, s0="normal", seed=seed, device=DEV,
+                               gate_logits=gate_logits)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_spec_verify_matches_oracle(dt, dk, dv):
+    N, T, H = 6, 5, 3
+    announce("spec verify", dt, dk, dv)
+    ins = _spec_inputs(N, T, H, dk, dv, dt, seed=dk * 3 + dv)
+    S = ins["S0"].clone()
+    o = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, ins["S0"])            # the checkpoint is only read
+    o_ref, _ = _oracle(ins)
+    e = rel_err(o.cpu().numpy(), o_ref)
+    announce("err_o %.3g" % e)
+    assert e <= 1e-4                             # fp32 steps on exactly widened inputs
+
+
+def test_spec_verify_equals_decode_steps_and_bf16_output():
+    N, T, H, dk, dv = 4, 7, 2, 128, 128
+    announce("spec verify vs decode", N, T, H)
+    ins = _spec_inputs(N, T, H, dk, dv, "bf16", seed=5)
+    o = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"])
+    ob = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"],
+                                 out_dtype=torch.bfloat16)
+    S = ins["S0"].clone()
+    steps = []
+    for t in range(T):
+        steps.append(binding.kda_decode_step(ins["q"][:, t].contiguous(), ins["k"][:, t].contiguous(),
+                                             ins["v"][:, t].contiguous(), ins["g"][:, t].contiguous(),
+                                             ins["beta"][:, t].contiguous(), S))
+    torch.cuda.synchronize()
+    od = torch.stack(steps, 1)
+    e = rel_err(o.cpu().numpy(), od.cpu().numpy())
+    announce("verify vs decode %.3g" % e)
+    assert e <= 1e-6
+    assert torch.equal(ob, o.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_spec_commit_replays_the_accepted_prefix(dt):
+    N, T, H, dk, dv = 8, 6, 3, 128, 128
+    announce("spec commit", dt)
+    ins = _spec_inputs(N, T, H, dk, dv, dt, seed=17)
+    acc_list = [0, 1, T, 3, T + 4, -2, 2, 5]       # out-of-range values clamp to [0, T]
+    accepted = torch.tensor(acc_list, dtype=torch.int32, device=DEV)
+    S = ins["S0"].clone()
+    binding.kda_spec_commit(ins["k"], ins["v"], ins["g"], ins["beta"], S, accepted)
+    torch.cuda.synchronize()
+    for n, a in enumerate(acc_list):
+        a = min(max(a, 0), T)
+        if a == 0:
+            assert torch.equal(S[n], ins["S0"][n])
+            continue
+        one = {m: ins[m][n:n + 1, :a].contiguous() for m in ("q", "k", "v", "g", "beta")}
+        one["S0"] = ins["S0"][n:n + 1]
+        _, S_ref = _oracle(one)
+        e = rel_err(S[n].cpu().numpy(), S_ref[0])
+        assert e <= 1e-4, (n, a, e)
+
+
+def test_spec_round_trip_equals_plain_decoding():
+    # verify 6 drafts, accept a per-request prefix, commit; then decode the
+    # next token: same outputs and state as decoding the accepted tokens and
+    # that next token one by one.
+    N, T, H, dk, dv = 5, 6, 2, 128, 128
+    announce("spec round trip")
+    ins = _spec_inputs(N, T, H, dk, dv, "bf16", seed=23)
+    nxt = inputs.make_decode(N, 1, H, dk, dv, "bf16", seed=24, device=DEV)
+    acc = [2, 0, 6, 4, 1]
+    S = ins["S0"].clone()
+    binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], S)
+    binding.kda_spec_commit(ins["k"], ins["v"], ins["g"], ins["beta"], S,
+                            torch.tensor(acc, dtype=torch.int32, device=DEV))
+    o_next = binding.kda_decode_step(nxt["q"][0], nxt["k"][0], nxt["v"][0], nxt["g"][0],
+                                     nxt["beta"][0], S)
+    S2 = ins["S0"].clone()
+    for n, a in enumerate(acc):
+        for t in range(a):
+            sl = lambda x: x[n:n + 1, t].contiguous()
+            binding.kda_decode_step(sl(ins["q"]), sl(ins["k"]), sl(ins["v"]), sl(ins["g"]),
+                                    sl(ins["beta"]), S2[n:n + 1])
+    o_next2 = binding.kda_decode_step(nxt["q"][0], nxt["k"][0], nxt["v"][0], nxt["g"][0],
+                                      nxt["beta"][0], S2)
+    torch.cuda.synchronize()
+    assert rel_err(S.cpu().numpy(), S2.cpu().numpy()) <= 1e-6
+    assert rel_err(o_next.cpu().numpy(), o_next2.cpu().numpy()) <= 1e-6
+
+
+def test_spec_empty_and_zero_accept():
+    ins = _spec_inputs(3, 4, 2, 64, 64, "bf16", seed=1)
+    S = ins["S0"].clone()
+    binding.kda_spec_commit(ins["k"], ins["v"], ins["g"], ins["beta"], S,
+                            torch.zeros(3, dtype=torch.int32, device=DEV))
+    e = _spec_inputs(3, 0, 2, 64, 64, "bf16", seed=1)
+    o = binding.kda_spec_verify(e["q"], e["k"], e["v"], e["g"], e["beta"], S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, ins["S0"]) and o.shape == (3, 0, 2, 64)
+
+
+# ---------------------------------------------------------------- sigmoid gate
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_chunk_fwd_sigmoid_gate_matches_oracle(dt):
+    announce("sigmoid gate forward", dt)
+    ins = inputs.make_forward(2, 300, 3, 128, 128, dt, s0="normal", seed=41, device=DEV,
+                              gate_logits=True)
+    o, ST, _ = binding.kda_chunk_fwd_ex(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                        ins["S0"], gate=SIG)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(ins, gate=c_oracle.GATE_SIGMOID)
+    eo, es = rel_err(o.cpu().numpy(), o_ref), rel_err(ST.cpu().numpy(), S_ref)
+    announce("err_o=%.3g err_S=%.3g" % (eo, es))
+    assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+def test_sigmoid_gate_limits_equal_the_log_decay_bounds():
+    # logits of +-1e30 give log-decays of exactly -5 and 0 on the GPU as well
+    ins = inputs.make_forward(1, 77, 2, 128, 64, "bf16", s0="normal", seed=43, device=DEV)
+    sign = torch.where(torch.rand(ins["g"].shape, device=DEV) < 0.5, 1.0, -1.0)
+    x = (sign * 1e30).to(torch.bfloat16)
+    g = torch.where(sign > 0, -5.0, 0.0).to(torch.bfloat16)
+    o1, S1, _ = binding.kda_chunk_fwd_ex(ins["q"], ins["k"], ins["v"], x, ins["beta"], ins["S0"],
+                                         gate=SIG)
+    o0, S0 = binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], g, ins["beta"], ins["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(S1, S0)
+
+
+def test_decode_and_spec_sigmoid_gate_match_oracle():
+    N, H, dk, dv = 6, 3, 128, 128
+    announce("sigmoid gate decode/spec")
+    d = inputs.make_decode(N, 3, H, dk, dv, "bf16", seed=47, device=DEV, gate_logits=True)
+    S = d["S"].clone()
+    outs = [binding.kda_decode_step_ex(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S,
+                                       gate=SIG) for s in range(3)]
+    torch.cuda.synchronize()
+    # the same 3 tokens as a [N, 3, H, d] draft for verify
+    ins = {n: d[n].transpose(0, 1).contiguous() for n in ("q", "k", "v", "g", "beta")}
+    ins["S0"] = d["S"]
+    o_ver = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], d["S"],
+                                    gate=SIG)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(ins, gate=c_oracle.GATE_SIGMOID)
+    o_dec = torch.stack(outs, 1).cpu().numpy()
+    assert rel_err(o_dec, o_ref) <= 1e-4
+    assert rel_err(S.cpu().numpy(), S_ref) <= 1e-4
+    assert rel_err(o_ver.cpu().numpy(), o_ref) <= 1e-4

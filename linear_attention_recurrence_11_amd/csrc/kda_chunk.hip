@@ -75,11 +75,14 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
   constexpr bool F32 = Path<InT>::kF32;
   constexpr int NM = DK / 16;
   constexpr int LDK = DK + 4;  // padded LDS row (conflict-free transposed reads)
+  using Op = typename Path<InT>::Op;
+  // Kt and Kb are staged in the state-pass operand type (fp16 for bf16
+  // inputs: both are rounded to it on use anyway), which keeps the LDS of
+  // this one-wave workgroup small enough for 4 waves per SIMD.
   __shared__ float s_beta[16];
-  __shared__ float s_kt[16 * LDK];
-  __shared__ float s_kb[16 * LDK];
+  __shared__ Op s_kt[16 * LDK];
+  __shared__ Op s_kb[16 * LDK];
   __shared__ float s_A[16][17];
-  __shared__ float s_M[16][17];
   __shared__ float s_T[16][17];
 
   const int l = threadIdx.x, c16 = l & 15, gq = l >> 4;
@@ -92,94 +95,112 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
   const bool valid = t < T;
   const size_t tok = static_cast<size_t>((b * T + (valid ? t : 0)) * H + h);
 
-  // ---- load this lane's token: 4*NM channels of q, k, g ----
-  float xq[NM][4], xk[NM][4], xg[NM][4];
+  uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NC + n) * L.bytes;
+
+  // ---- load this lane's token: 4*NM channels of q, k, g, kept packed ----
+  // (converted where used, so the whole chunk's fp32 operands are never live
+  // at once; bf16 inputs take 2 VGPRs per 4 channels)
+  using Raw = typename std::conditional<F32, float4, uint2>::type;
+  Raw rq[NM], rk[NM], rg[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const size_t off = tok * DK + 16 * m + 4 * gq;
     if (valid) {
-      load_in4(q, off, xq[m]);
-      load_in4(k, off, xk[m]);
-      load_in4(g, off, xg[m]);
+      rq[m] = *reinterpret_cast<const Raw*>(q + off);
+      rk[m] = *reinterpret_cast<const Raw*>(k + off);
+      rg[m] = *reinterpret_cast<const Raw*>(g + off);
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xq[m][i] = xk[m][i] = xg[m][i] = 0.f;
+      rq[m] = rk[m] = rg[m] = Raw{};
     }
   }
   if (gq == 0) s_beta[c16] = valid ? load_in(beta, tok) : 0.f;
 
-  // ---- per-channel cumulative log-decay over the chunk (base 2) ----
-  float E[NM][4], Eh[NM][4], Eb[NM][4];
+  // ---- per pair of 16-channel groups: decay scan, scaled operands, Gram ----
+  // Channel (m, i) = 16m + 4gq + i. The Gram contraction over the 8 channels
+  // of pair p takes slot j = 4(m - 2p) + i (any bijection serves a Gram
+  // product); the same slots order the Qt record (state-pass layout).
+  // MrawT = Kh Qt^T is M^T: its output layout puts M[c16][4gq + i] in this
+  // lane, the layout the record wants, with no transpose through LDS.
+  f32x4 Araw = zero4(), MrawT = zero4();
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
+  for (int p = 0; p < NM / 2; ++p) {
+    float qt[8], kt[8], kh[8], eg[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // padded tokens past T carry log-decay 0 whatever the gate
-      const float x = (valid ? gate_decay<GATE>(xg[m][i]) : 0.f) * kLog2e;
-      const float G = row_inclusive_prefix_sum(x);    // log2 e^Gamma_r
-      const float Gb = row_exclusive_suffix_sum(x);   // log2 e^(gamma - Gamma_r)
-      E[m][i] = exp2f(G);
-      Eh[m][i] = exp2f(-G);
-      Eb[m][i] = exp2f(Gb);
-    }
-  }
-
-  // ---- scaled operands ----
-  float qt[NM][4], kt[NM][4], kh[NM][4];
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qt[m][i] = E[m][i] * xq[m][i];
-      kt[m][i] = E[m][i] * xk[m][i];
-      kh[m][i] = Eh[m][i] * xk[m][i];
-      s_kt[c16 * LDK + 16 * m + 4 * gq + i] = kt[m][i];
-      s_kb[c16 * LDK + 16 * m + 4 * gq + i] = Eb[m][i] * xk[m][i];
-    }
-  }
-
-  // ---- chunk Gram tiles: Araw = Kt Kh^T, Mraw = Qt Kh^T (16 x 16) ----
-  f32x4 Araw = zero4(), Mraw = zero4();
-  if constexpr (F32) {
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int jj = 0; jj < 2; ++jj) {
+      const int m = 2 * p + jj;
+      float xq[4], xk[4], xg[4];
+      unpack4(rq[m], xq);
+      unpack4(rk[m], xk);
+      unpack4(rg[m], xg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Araw = mma_16x16x4_f32(kt[m][i], kh[m][i], Araw);
-        Mraw = mma_16x16x4_f32(qt[m][i], kh[m][i], Mraw);
+        // padded tokens past T carry log-decay 0 whatever the gate
+        const float x = (valid ? gate_decay<GATE>(xg[i]) : 0.f) * kLog2e;
+        const float G = row_inclusive_prefix_sum(x);    // log2 e^Gamma_r
+        const float Gb = row_exclusive_suffix_sum(x);   // log2 e^(gamma - Gamma_r)
+        // the -5 floor bounds |G|, |Gb| by 80 log2(e) over 16 tokens, so every
+        // power of two here is a normal float: the hardware exp2 needs no
+        // range reduction
+        const float E = __builtin_amdgcn_exp2f(G);
+        const float Eh = __builtin_amdgcn_exp2f(-G);
+        const float Eb = __builtin_amdgcn_exp2f(Gb);
+        const int j = 4 * jj + i;
+        qt[j] = E * xq[i];
+        kt[j] = E * xk[i];
+        kh[j] = Eh * xk[i];
+        eg[j] = E;
+        s_kt[c16 * LDK + 16 * m + 4 * gq + i] = static_cast<Op>(kt[j]);
+        s_kb[c16 * LDK + 16 * m + 4 * gq + i] = static_cast<Op>(Eb * xk[i]);
       }
-  } else {
-    // bf16 operands carry the e^{+-Gamma} range; each is split into a bf16
-    // high part and a bf16 remainder (hi*hi + hi*lo + lo*hi) for accuracy.
-#pragma unroll
-    for (int p = 0; p < NM / 2; ++p) {
-      bf16x8 kt_hi, kt_lo, kh_hi, kh_lo, qt_hi, qt_lo;
+    }
+    if constexpr (F32) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int m = 2 * p + (j >> 2), i = j & 3;
-        kt_hi[j] = static_cast<__bf16>(kt[m][i]);
-        kt_lo[j] = static_cast<__bf16>(kt[m][i] - static_cast<float>(kt_hi[j]));
-        kh_hi[j] = static_cast<__bf16>(kh[m][i]);
-        kh_lo[j] = static_cast<__bf16>(kh[m][i] - static_cast<float>(kh_hi[j]));
-        qt_hi[j] = static_cast<__bf16>(qt[m][i]);
-        qt_lo[j] = static_cast<__bf16>(qt[m][i] - static_cast<float>(qt_hi[j]));
+        Araw = mma_16x16x4_f32(kt[j], kh[j], Araw);
+        MrawT = mma_16x16x4_f32(kh[j], qt[j], MrawT);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const size_t off = static_cast<size_t>((2 * p + jj) * 64 + l) * 16;
+        *reinterpret_cast<float4*>(rec + L.q + off) =
+            make_float4(qt[4 * jj], qt[4 * jj + 1], qt[4 * jj + 2], qt[4 * jj + 3]);
+      }
+    } else {
+      // bf16 operands carry the e^{+-Gamma} range; each is split into a bf16
+      // high part and a bf16 remainder (hi*hi + hi*lo + lo*hi) for accuracy.
+      bf16x8 kt_hi, kt_lo, kh_hi, kh_lo, qt_hi, qt_lo;
+      f16x8 qv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kt_hi[j] = static_cast<__bf16>(kt[j]);
+        kt_lo[j] = static_cast<__bf16>(kt[j] - static_cast<float>(kt_hi[j]));
+        kh_hi[j] = static_cast<__bf16>(kh[j]);
+        kh_lo[j] = static_cast<__bf16>(kh[j] - static_cast<float>(kh_hi[j]));
+        qt_hi[j] = static_cast<__bf16>(qt[j]);
+        qt_lo[j] = static_cast<__bf16>(qt[j] - static_cast<float>(qt_hi[j]));
+        qv[j] = static_cast<Op>(qt[j]);
       }
       Araw = mma_16x16x32_bf16(kt_hi, kh_hi, Araw);
       Araw = mma_16x16x32_bf16(kt_hi, kh_lo, Araw);
       Araw = mma_16x16x32_bf16(kt_lo, kh_hi, Araw);
-      Mraw = mma_16x16x32_bf16(qt_hi, kh_hi, Mraw);
-      Mraw = mma_16x16x32_bf16(qt_hi, kh_lo, Mraw);
-      Mraw = mma_16x16x32_bf16(qt_lo, kh_hi, Mraw);
+      MrawT = mma_16x16x32_bf16(kh_hi, qt_hi, MrawT);
+      MrawT = mma_16x16x32_bf16(kh_lo, qt_hi, MrawT);
+      MrawT = mma_16x16x32_bf16(kh_hi, qt_lo, MrawT);
+      *reinterpret_cast<f16x8*>(rec + L.q + static_cast<size_t>(p * 64 + l) * 16) = qv;
+    }
+    if (c16 == 15) {  // e^gamma for this lane's channels of the pair
+      float* egp = reinterpret_cast<float*>(rec + L.eg) + gq * (DK / 4) + 8 * p;
+      *reinterpret_cast<float4*>(egp) = make_float4(eg[0], eg[1], eg[2], eg[3]);
+      *reinterpret_cast<float4*>(egp + 4) = make_float4(eg[4], eg[5], eg[6], eg[7]);
     }
   }
   __syncthreads();  // s_beta, s_kt, s_kb visible
 
-  // ---- masks: A strictly lower with row scale beta_r, M lower incl. diag ----
+  // ---- mask: A strictly lower with row scale beta_r ----
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * gq + i, s = c16;
     s_A[r][s] = (s < r) ? s_beta[r] * Araw[i] : 0.f;
-    s_M[r][s] = (s <= r) ? Mraw[i] : 0.f;
   }
   __syncthreads();
 
@@ -201,19 +222,21 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
   }
   __syncthreads();
 
+  // tb[i] = Tm[c16][s] beta_s and mf[i] = M[c16][s] (M lower incl. diag)
+  // for s = 4gq + i: this lane's fragments of the record
   float tb[4], mf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s = 4 * gq + i;
     tb[i] = s_T[c16][s] * s_beta[s];
-    mf[i] = s_M[c16][s];
+    mf[i] = (s <= c16) ? MrawT[i] : 0.f;
   }
 
   // ---- W^T tiles = Kt^T (diag(beta) Tm^T): lane gets W[c16][16m+4gq+i] ----
   float w[NM][4];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    float a[4];
+    Op a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = s_kt[(4 * gq + i) * LDK + 16 * m + c16];
     f32x4 acc = zero4();
@@ -224,7 +247,7 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
       f16x4 av, bv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        av[i] = static_cast<_Float16>(a[i]);
+        av[i] = a[i];
         bv[i] = static_cast<_Float16>(tb[i]);
       }
       acc = mma_16x16x16_f16(av, bv, acc);
@@ -233,15 +256,12 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
     for (int i = 0; i < 4; ++i) w[m][i] = acc[i];
   }
 
-  // ---- write the record ----
-  uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NC + n) * L.bytes;
-  using Op = typename Path<InT>::Op;
+  // ---- write the rest of the record ----
   if constexpr (F32) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const size_t off = static_cast<size_t>(m * 64 + l) * 16;
       *reinterpret_cast<float4*>(rec + L.w + off) = make_float4(-w[m][0], -w[m][1], -w[m][2], -w[m][3]);
-      *reinterpret_cast<float4*>(rec + L.q + off) = make_float4(qt[m][0], qt[m][1], qt[m][2], qt[m][3]);
       float kb4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) kb4[i] = s_kb[(4 * gq + i) * LDK + 16 * m + c16];
@@ -252,22 +272,16 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
   } else {
 #pragma unroll
     for (int p = 0; p < NM / 2; ++p) {
-      f16x8 wv, qv;
+      f16x8 wv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int m = 2 * p + (j >> 2), i = j & 3;
-        wv[j] = static_cast<Op>(-w[m][i]);
-        qv[j] = static_cast<Op>(qt[m][i]);
-      }
-      const size_t off = static_cast<size_t>(p * 64 + l) * 16;
-      *reinterpret_cast<f16x8*>(rec + L.w + off) = wv;
-      *reinterpret_cast<f16x8*>(rec + L.q + off) = qv;
+      for (int j = 0; j < 8; ++j) wv[j] = static_cast<Op>(-w[2 * p + (j >> 2)][j & 3]);
+      *reinterpret_cast<f16x8*>(rec + L.w + static_cast<size_t>(p * 64 + l) * 16) = wv;
     }
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       f16x4 kv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kv[i] = static_cast<Op>(s_kb[(4 * gq + i) * LDK + 16 * m + c16]);
+      for (int i = 0; i < 4; ++i) kv[i] = s_kb[(4 * gq + i) * LDK + 16 * m + c16];
       *reinterpret_cast<f16x4*>(rec + L.kbar + static_cast<size_t>(m * 64 + l) * 8) = kv;
     }
     f16x4 mh, ml, tv;
@@ -280,12 +294,6 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
     *reinterpret_cast<f16x4*>(rec + L.m + l * 8) = mh;
     *reinterpret_cast<f16x4*>(rec + L.m + 512 + l * 8) = ml;
     *reinterpret_cast<f16x4*>(rec + L.tb + l * 8) = tv;
-  }
-  if (c16 == 15) {  // e^gamma for this lane's channels
-    float* eg = reinterpret_cast<float*>(rec + L.eg) + gq * (DK / 4);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-      *reinterpret_cast<float4*>(eg + 4 * m) = make_float4(E[m][0], E[m][1], E[m][2], E[m][3]);
   }
 }
 

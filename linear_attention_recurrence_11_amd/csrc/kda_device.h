@@ -48,6 +48,18 @@ template <> __device__ __forceinline__ void load_in4<uint16_t>(const uint16_t* p
   out[3] = __uint_as_float(x.y & 0xffff0000u);
 }
 
+// Unpack four input elements loaded as one vector (float4 for fp32 inputs,
+// two dwords of bf16 bit pairs for bf16 inputs).
+__device__ __forceinline__ void unpack4(const float4& x, float out[4]) {
+  out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+}
+__device__ __forceinline__ void unpack4(const uint2& x, float out[4]) {
+  out[0] = __uint_as_float(x.x << 16);
+  out[1] = __uint_as_float(x.x & 0xffff0000u);
+  out[2] = __uint_as_float(x.y << 16);
+  out[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
 template <typename T> __device__ __forceinline__ void store_out(T* p, size_t i, float x);
 template <> __device__ __forceinline__ void store_out<float>(float* p, size_t i, float x) { p[i] = x; }
 template <> __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, size_t i, float x) {

@@ -314,54 +314,111 @@ struct ChunkFrags {
   float vv[4];
 
   // Record fragments of one chunk; `rec` is uniform across the wavefront, so
-  // every address is a scalar base plus a fixed per-lane offset.
+  // every access is a scalar base plus a 32-bit per-lane byte offset.
   __device__ __forceinline__ void load_record(const uint8_t* rec, const RecordLayout& L, int l,
                                               int gq) {
+    const uint8_t* rw = rec + L.w;
+    const uint8_t* rq = rec + L.q;
+    const uint8_t* rk = rec + L.kbar;
+    const uint8_t* rm = rec + L.m;
+    const uint8_t* rt = rec + L.tb;
+    const uint8_t* re = rec + L.eg;
     if constexpr (F32) {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint32_t off = static_cast<uint32_t>(m * 64 + l) * 16;
-        w[m] = *reinterpret_cast<const f32x4*>(rec + L.w + off);
-        q[m] = *reinterpret_cast<const f32x4*>(rec + L.q + off);
-        kb[m] = *reinterpret_cast<const f32x4*>(rec + L.kbar + off);
+        w[m] = ld_at<f32x4>(rw, off);
+        q[m] = ld_at<f32x4>(rq, off);
+        kb[m] = ld_at<f32x4>(rk, off);
       }
-      mh = *reinterpret_cast<const f32x4*>(rec + L.m + l * 16);
-      tb = *reinterpret_cast<const f32x4*>(rec + L.tb + l * 16);
+      mh = ld_at<f32x4>(rm, static_cast<uint32_t>(l) * 16);
+      tb = ld_at<f32x4>(rt, static_cast<uint32_t>(l) * 16);
     } else {
 #pragma unroll
       for (int p = 0; p < NM / 2; ++p) {
         const uint32_t off = static_cast<uint32_t>(p * 64 + l) * 16;
-        w[p] = *reinterpret_cast<const f16x8*>(rec + L.w + off);
-        q[p] = *reinterpret_cast<const f16x8*>(rec + L.q + off);
+        w[p] = ld_at<f16x8>(rw, off);
+        q[p] = ld_at<f16x8>(rq, off);
       }
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-        kb[m] = *reinterpret_cast<const f16x4*>(rec + L.kbar + static_cast<uint32_t>(m * 64 + l) * 8);
-      mh = *reinterpret_cast<const f16x4*>(rec + L.m + l * 8);
-      ml = *reinterpret_cast<const f16x4*>(rec + L.m + 512 + l * 8);
-      tb = *reinterpret_cast<const f16x4*>(rec + L.tb + l * 8);
+      for (int m = 0; m < NM; ++m) kb[m] = ld_at<f16x4>(rk, static_cast<uint32_t>(m * 64 + l) * 8);
+      mh = ld_at<f16x4>(rm, static_cast<uint32_t>(l) * 8);
+      ml = ld_at<f16x4>(rm, 512u + static_cast<uint32_t>(l) * 8);
+      tb = ld_at<f16x4>(rt, static_cast<uint32_t>(l) * 8);
     }
-    const f32x4* egp = reinterpret_cast<const f32x4*>(rec + L.eg) + gq * NM;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) eg[m] = egp[m];
+    for (int m = 0; m < NM; ++m) eg[m] = ld_at<f32x4>(re, static_cast<uint32_t>(gq * NM + m) * 16);
   }
 
   // V rows 4gq + i of a chunk; `vchunk` (uniform) points at the chunk's first
-  // token of this (b, h), voff[i] = (4gq + i) * H * DV + col. Tokens at or
-  // past `valid` (a last partial chunk) read as zero.
-  __device__ __forceinline__ void load_v(const InT* vchunk, const uint32_t voff[4]) {
+  // token of this (b, h), vb[i] = ((4gq + i) * H * DV + col) * sizeof(InT)
+  // (byte offsets). Tokens at or past `valid` (a last partial chunk) read as
+  // zero.
+  __device__ __forceinline__ void load_v(const InT* vchunk, const uint32_t vb[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = load_in(vchunk, voff[i]);
+    for (int i = 0; i < 4; ++i) vv[i] = ld_in_at(vchunk, vb[i]);
   }
-  __device__ __forceinline__ void load_v_partial(const InT* vchunk, const uint32_t voff[4], int gq,
+  __device__ __forceinline__ void load_v_partial(const InT* vchunk, const uint32_t vb[4], int gq,
                                                  int valid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = (4 * gq + i < valid) ? load_in(vchunk, voff[i]) : 0.f;
+    for (int i = 0; i < 4; ++i) vv[i] = (4 * gq + i < valid) ? ld_in_at(vchunk, vb[i]) : 0.f;
   }
 };
 
 // One chunk of the sequential pass on a dk x 16 state slice S (output layout):
 // U = Tb V - W S,  O = Qt S + M U,  S <- Diag(e^gamma) S + Kb^T U.  Returns O.
+// One chunk of the sequential pass on the fp16-operand path, with the
+// chunk's V rows 4gq + i (column c16) given in fp16.
+template <typename InT, int DK>
+__device__ __forceinline__ f32x4 chunk_step_h(const ChunkFrags<InT, DK>& cur, f16x4 v16,
+                                            f32x4 (&S)[DK / 16]) {
+  constexpr int NM = DK / 16;
+  f32x4 U, O;
+  // Every accumulation chain below uses one MFMA shape (16x16x32). Two shapes
+  // chained through an accumulator need wait states on gfx950 that the
+  // compiler does not insert; the 16-deep token contractions are issued as
+  // 16x16x32 with the upper 16 slots zero (or, for M U, holding the
+  // low-order part of M against a second copy of U). K=16 and K=32 issue at
+  // the same rate on gfx950, so the padding costs nothing.
+  f16x8 tbz, vz;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tbz[i] = cur.tb[i];
+    tbz[i + 4] = static_cast<_Float16>(0.f);
+    vz[i] = v16[i];
+    vz[i + 4] = static_cast<_Float16>(0.f);
+  }
+  U = mma_16x16x32_f16(tbz, vz, zero4());                                    // Ut = Tb V
+  f16x8 sh[NM / 2];
+#pragma unroll
+  for (int p = 0; p < NM / 2; ++p)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
+  O = zero4();
+#pragma unroll
+  for (int p = 0; p < NM / 2; ++p) {
+    U = mma_16x16x32_f16(cur.w[p], sh[p], U);                                // U = Ut - W S
+    O = mma_16x16x32_f16(cur.q[p], sh[p], O);                                // O = Qt S
+  }
+  f16x8 uu, mhl;
+  f16x4 u4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 x = static_cast<_Float16>(U[i]);
+    uu[i] = x;
+    uu[i + 4] = x;
+    u4[i] = x;
+    mhl[i] = cur.mh[i];
+    mhl[i + 4] = cur.ml[i];
+  }
+  O = mma_16x16x32_f16(mhl, uu, O);                                          // O += (Mhi + Mlo) U
+  // S = Diag(e^gamma) S + Kb^T U: the accumulator input is the VALU product
+  // S * e^gamma, never another MFMA's output, so the 16x16x16 shape is safe.
+#pragma unroll
+  for (int m = 0; m < NM; ++m) S[m] = mma_16x16x16_f16(cur.kb[m], u4, S[m] * cur.eg[m]);
+  return O;
+}
+
 template <typename InT, int DK>
 __device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<InT, DK>& cur, f32x4 (&S)[DK / 16]) {
   constexpr int NM = DK / 16;
@@ -387,48 +444,10 @@ __device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<InT, DK>& cur, f32x
       for (int i = 0; i < 4; ++i) S[m] = mma_16x16x4_f32(cur.kb[m][i], U[i], S[m]);
     }
   } else {
-    // Every accumulation chain below uses one MFMA shape (16x16x32). Two shapes
-    // chained through an accumulator need wait states on gfx950 that the
-    // compiler does not insert; the 16-deep token contractions are issued as
-    // 16x16x32 with the upper 16 slots zero (or, for M U, holding the
-    // low-order part of M against a second copy of U). K=16 and K=32 issue at
-    // the same rate on gfx950, so the padding costs nothing.
-    f16x8 tbz, vz;
+    f16x4 v16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tbz[i] = cur.tb[i];
-      tbz[i + 4] = static_cast<_Float16>(0.f);
-      vz[i] = static_cast<_Float16>(cur.vv[i]);
-      vz[i + 4] = static_cast<_Float16>(0.f);
-    }
-    U = mma_16x16x32_f16(tbz, vz, zero4());                                    // Ut = Tb V
-    f16x8 sh[NM / 2];
-#pragma unroll
-    for (int p = 0; p < NM / 2; ++p)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
-    O = zero4();
-#pragma unroll
-    for (int p = 0; p < NM / 2; ++p) {
-      U = mma_16x16x32_f16(cur.w[p], sh[p], U);                                // U = Ut - W S
-      O = mma_16x16x32_f16(cur.q[p], sh[p], O);                                // O = Qt S
-    }
-    f16x8 uu, mhl;
-    f16x4 u4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 x = static_cast<_Float16>(U[i]);
-      uu[i] = x;
-      uu[i + 4] = x;
-      u4[i] = x;
-      mhl[i] = cur.mh[i];
-      mhl[i + 4] = cur.ml[i];
-    }
-    O = mma_16x16x32_f16(mhl, uu, O);                                          // O += (Mhi + Mlo) U
-    // S = Diag(e^gamma) S + Kb^T U: the accumulator input is the VALU product
-    // S * e^gamma, never another MFMA's output, so the 16x16x16 shape is safe.
-#pragma unroll
-    for (int m = 0; m < NM; ++m) S[m] = mma_16x16x16_f16(cur.kb[m], u4, S[m] * cur.eg[m]);
+    for (int i = 0; i < 4; ++i) v16[i] = static_cast<_Float16>(cur.vv[i]);
+    O = chunk_step_h(cur, v16, S);
   }
   return O;
 }
@@ -472,9 +491,15 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
   const InT* vb = v + hb;
   OutT* ob = o + hb;
   const size_t chunk_elems = static_cast<size_t>(16 * H) * DV;
-  uint32_t toff[4];
+  // per-lane byte offsets of rows 4gq + i of a chunk (H * DV <= 2^25, so
+  // 16 * H * DV elements of at most 4 bytes fit in 32 bits)
+  uint32_t vbo[4], obo[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) toff[i] = static_cast<uint32_t>((4 * gq + i) * H * DV + col);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t e = static_cast<uint32_t>((4 * gq + i) * H * DV + col);
+    vbo[i] = e * static_cast<uint32_t>(sizeof(InT));
+    obo[i] = e * static_cast<uint32_t>(sizeof(OutT));
+  }
 
   const int64_t NF = T / 16;  // full chunks
   // Full chunks: records prefetched two chunks ahead (fp32 path: one) into
@@ -484,7 +509,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
   auto fetch = [&](Frags& f, int64_t c) __attribute__((always_inline)) {
     c = c < NF - 1 ? c : NF - 1;
     f.load_record(rec0 + static_cast<size_t>(c) * L.bytes, L, l, gq);
-    f.load_v(vb + static_cast<size_t>(c) * chunk_elems, toff);
+    f.load_v(vb + static_cast<size_t>(c) * chunk_elems, vbo);
   };
   // Snapshots (snap_chunks > 0): the state after every snap_chunks full
   // chunks, i.e. after tokens [0, (j+1) * 16 * snap_chunks), goes to snapshot
@@ -503,7 +528,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
   auto finish = [&](int64_t n, f32x4 O) __attribute__((always_inline)) {
     OutT* oc = ob + static_cast<size_t>(n) * chunk_elems;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store_out(oc, toff[i], O[i]);
+    for (int i = 0; i < 4; ++i) st_out_at(oc, obo[i], O[i]);
     if (n + 1 == next_snap) {
       float* sp = snap_b + static_cast<size_t>(n / snap_chunks) * H * DK * DV;
 #pragma unroll
@@ -543,13 +568,250 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
     const int valid = static_cast<int>(T - NF * 16);
     Frags f;
     f.load_record(rec0 + static_cast<size_t>(NF) * L.bytes, L, l, gq);
-    f.load_v_partial(vb + static_cast<size_t>(NF) * chunk_elems, toff, gq, valid);
+    f.load_v_partial(vb + static_cast<size_t>(NF) * chunk_elems, vbo, gq, valid);
     const f32x4 O = chunk_step(f, S);
     OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (4 * gq + i < valid) store_out(oc, toff[i], O[i]);
+      if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
   }
+  if (ST) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ST[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] = S[m][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sequential state pass, fp16-operand path: a loader wave and a compute wave.
+//
+// The sequential chain (U = Ut - W S, S <- Diag(e^gamma) S + Kb^T U) runs on
+// one wavefront per (b, h, 16-column slice). Fed from global memory directly,
+// that wavefront waits on its own prefetch loads: the compiler's wait
+// placement in an unrolled prefetch loop leaves only about one chunk of
+// loads in flight, and HBM latency then sets the pace. Here a second
+// wavefront of the same workgroup streams each chunk's record and V tile
+// from HBM into a ring of LDS slots, several chunks ahead, with coalesced
+// 16-byte loads (and converts V to fp16, transposed for the MFMA operand);
+// the compute wavefront only reads LDS. One LDS-only barrier per chunk keeps
+// the two in step:
+//   before the loop  slots hold chunks 0 .. kRing-2;
+//   step n           compute reads slot n % kRing (and prefetches the next
+//                    slot); the loader fills slot (n + kRing - 1) % kRing,
+//                    which the compute wave last read at step n - 1.
+// The loader keeps kStages chunks of loads in registers, so each chunk's
+// loads are issued kStages steps before they are written to LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kRing = 4;
+constexpr int kStages = 3;
+
+// LDS-only release/acquire around a workgroup barrier: orders this wave's LDS
+// accesses against the other wave's, without waiting for global loads.
+// The scheduling barriers keep the instruction scheduler from moving work
+// across steps (it would otherwise hoist the loader's use of loaded data to
+// the top of the loop, where it must wait for every load in flight).
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int DK>
+struct RingGeom {
+  static constexpr int kRec = DK == 128 ? 14336 : 8192;  // record bytes (bf16 inputs)
+  static constexpr int kUnits = kRec / 1024;             // 16-byte loads per lane
+  static constexpr int kSlot = kRec + 512;               // + V^T tile, 16x16 fp16
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DK>
+struct LoaderStage {
+  u32x4 r[RingGeom<DK>::kUnits];
+  u32x2 v;
+  bool v_ok;  // the V token exists (applied at commit: a select right after
+              // the load would make the compiler wait for it there)
+};
+
+template <typename OutT, int DK>
+__global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __restrict__ v,
+                                                           const uint8_t* __restrict__ ws,
+                                                           const float* S0, OutT* __restrict__ o,
+                                                           float* ST, float* __restrict__ snap,
+                                                           int64_t snap_chunks, int64_t T, int64_t H,
+                                                           int64_t DV, int64_t NC, int64_t nslices,
+                                                           int64_t nheads, RecordLayout L) {
+  using G = RingGeom<DK>;
+  constexpr int NM = DK / 16;
+  using Frags = ChunkFrags<uint16_t, DK>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * G::kSlot];
+
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, c16 = l & 15, gq = l >> 4;
+  // XCD-aware numbering, as in kda_state_pass.
+  const int64_t wgid = blockIdx.x;
+  const int64_t xcd = wgid & 7, kk = wgid >> 3;
+  const int64_t head = xcd + 8 * (kk / nslices);
+  const int64_t slice = kk % nslices;
+  if (head >= nheads) return;  // whole workgroup
+  const int64_t b = head / H, h = head % H;
+  const uint8_t* rec0 = ws + static_cast<size_t>(head) * NC * G::kRec;
+  const size_t hb = static_cast<size_t>(b * T * H + h) * DV;
+  const size_t chunk_elems = static_cast<size_t>(16 * H) * DV;
+  const int64_t NF = T / 16;
+  const int64_t NC3 = (NC + 2) / 3 * 3;  // loader steps (and barriers), a multiple of 3
+
+  if (wave == 0) {
+    // ---------------- loader ----------------
+    // V: lane -> token tv of the chunk, columns cv .. cv+3 of the slice.
+    const int tv = l >> 2, cv = 4 * (l & 3);
+    const uint32_t vcol = static_cast<uint32_t>(slice * 16 + cv);
+    const uint32_t vrow = static_cast<uint32_t>(H * DV);  // elements per token
+    const uint16_t* vb = v + hb;
+    // Loads are unconditional (chunks past the end re-read the last one, V
+    // tokens past T are zeroed by a select): a branch around them would make
+    // the compiler's wait counting conservative at the join.
+    auto issue = [&](LoaderStage<DK>& st, int64_t c) __attribute__((always_inline)) {
+      const int64_t cc = c < NC ? c : NC - 1;
+      const uint8_t* src = rec0 + static_cast<size_t>(cc) * G::kRec;
+#pragma unroll
+      for (int j = 0; j < G::kUnits; ++j) st.r[j] = ld_at<u32x4>(src, static_cast<uint32_t>(j * 64 + l) * 16);
+      // tokens past T (last partial chunk) read the last token instead: every
+      // load stays inside v; the value is zeroed at commit
+      const int64_t tmax = T - 1 - cc * 16;
+      const uint32_t t = static_cast<uint32_t>(tv < tmax ? tv : tmax);
+      st.v = ld_at<u32x2>(vb + static_cast<size_t>(cc) * chunk_elems, (t * vrow + vcol) * 2u);
+      st.v_ok = c * 16 + tv < T;
+    };
+    // Commits are unconditional too: a chunk past the end lands in a slot
+    // the compute wave reads no more (the same reuse distance as in the
+    // steady state), and is never read.
+    auto commit = [&](const LoaderStage<DK>& st, int64_t c) __attribute__((always_inline)) {
+      {
+        uint8_t* dst = ring + static_cast<int>(c % kRing) * G::kSlot;
+#pragma unroll
+        for (int j = 0; j < G::kUnits; ++j) st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[j]);
+        // V^T[col][token] in fp16: the compute lane (c16, gq) reads the four
+        // tokens 4gq .. 4gq+3 of column c16 as one 8-byte word.
+        const uint32_t v0 = st.v_ok ? st.v[0] : 0u, v1 = st.v_ok ? st.v[1] : 0u;
+        const float x[4] = {__uint_as_float(v0 << 16), __uint_as_float(v0 & 0xffff0000u),
+                            __uint_as_float(v1 << 16), __uint_as_float(v1 & 0xffff0000u)};
+        _Float16* vt = reinterpret_cast<_Float16*>(dst + G::kRec);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vt[(cv + i) * 16 + tv] = static_cast<_Float16>(x[i]);
+      }
+    };
+    LoaderStage<DK> s0, s1, s2;
+    issue(s0, 0);
+    issue(s1, 1);
+    issue(s2, 2);
+    commit(s0, 0);
+    issue(s0, 3);
+    commit(s1, 1);
+    issue(s1, 4);
+    commit(s2, 2);
+    issue(s2, 5);
+    ring_barrier();
+    // step n writes chunk n + 3 (slot (n - 1) % kRing) from stage n % 3 and
+    // refills that stage with chunk n + 6. The loop runs a multiple of 3
+    // steps with no exit in between (an exit inside would make the compiler
+    // drain every load at the loop's back edge); the compute wave pads its
+    // barriers to the same count.
+    for (int64_t n = 0; n < NC3; n += 3) {
+      commit(s0, n + 3);
+      issue(s0, n + 6);
+      ring_barrier();
+      commit(s1, n + 4);
+      issue(s1, n + 7);
+      ring_barrier();
+      commit(s2, n + 5);
+      issue(s2, n + 8);
+      ring_barrier();
+    }
+    return;
+  }
+
+  // ---------------- compute ----------------
+  const int64_t col = slice * 16 + c16;
+  f32x4 S[NM];
+  const size_t sbase = static_cast<size_t>(head) * DK * DV + col;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+  OutT* ob = o + hb;
+  uint32_t obo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    obo[i] = static_cast<uint32_t>((4 * gq + i) * H * DV + col) * static_cast<uint32_t>(sizeof(OutT));
+  int64_t next_snap = snap_chunks;
+  float* snap_b = nullptr;
+  if (snap_chunks > 0) {
+    const int64_t ns = NF / snap_chunks;
+    snap_b = snap + (static_cast<size_t>(b * ns) * H + h) * DK * DV + col;
+  }
+  auto finish = [&](int64_t n, f32x4 O) __attribute__((always_inline)) {
+    OutT* oc = ob + static_cast<size_t>(n) * chunk_elems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_out_at(oc, obo[i], O[i]);
+    if (n + 1 == next_snap) {
+      float* sp = snap_b + static_cast<size_t>(n / snap_chunks) * H * DK * DV;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[static_cast<size_t>(16 * m + 4 * gq + i) * DV] = S[m][i];
+      next_snap += snap_chunks;
+    }
+  };
+  auto read = [&](Frags& f, f16x4& vh, int64_t c) __attribute__((always_inline)) {
+    const uint8_t* src = ring + static_cast<int>(c % kRing) * G::kSlot;
+    f.load_record(src, L, l, gq);
+    vh = ld_at<f16x4>(src + G::kRec, static_cast<uint32_t>(c16 * 16 + 4 * gq) * 2);
+  };
+  ring_barrier();
+  Frags f0, f1;
+  f16x4 v0, v1;
+  read(f0, v0, 0);
+  // Full chunks, two per iteration (the fragment buffers alternate by
+  // position, never by copy); the next chunk's slot is read one step ahead.
+  int64_t n = 0;
+  for (; n + 1 < NF; n += 2) {
+    read(f1, v1, n + 1);
+    finish(n, chunk_step_h(f0, v0, S));
+    ring_barrier();
+    if (n + 2 < NC) read(f0, v0, n + 2);
+    finish(n + 1, chunk_step_h(f1, v1, S));
+    ring_barrier();
+  }
+  if (n < NF) {  // an odd last full chunk, in f0
+    if (n + 1 < NC) read(f1, v1, n + 1);
+    finish(n, chunk_step_h(f0, v0, S));
+    ring_barrier();
+    ++n;
+    if (NC > NF) {  // then the partial chunk, in f1
+      const int valid = static_cast<int>(T - NF * 16);
+      const f32x4 O = chunk_step_h(f1, v1, S);
+      OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
+      ring_barrier();
+    }
+  } else if (NC > NF) {  // even number of full chunks: the partial chunk is in f0
+    const int valid = static_cast<int>(T - NF * 16);
+    const f32x4 O = chunk_step_h(f0, v0, S);
+    OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
+    ring_barrier();
+  }
+  for (int64_t k = NC; k < NC3; ++k) ring_barrier();  // match the loader's steps
   if (ST) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -589,6 +851,15 @@ hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   const int64_t nheads = a.B * a.H;
   const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
   const int64_t snap_chunks = wants_snapshots(a) ? a.snapshot_every / 16 : 0;
+  if constexpr (!Path<InT>::kF32) {
+    if (L.bytes != RingGeom<DK>::kRec) return hipErrorInvalidValue;  // layout and ring disagree
+    hipLaunchKernelGGL((kda_state_pass_ring<OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(128), 0, stream, static_cast<const uint16_t*>(a.v),
+                       static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
+                       a.S_T, snap_chunks > 0 ? a.snapshots : nullptr, snap_chunks, a.T, a.H, a.dv,
+                       NC, nslices, nheads, L);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
                      dim3(64), 0, stream, static_cast<const InT*>(a.v),
                      static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),

@@ -60,6 +60,30 @@ __device__ __forceinline__ void unpack4(const uint2& x, float out[4]) {
   out[3] = __uint_as_float(x.y & 0xffff0000u);
 }
 
+// Access at a wavefront-uniform base plus a 32-bit per-lane byte offset. This
+// is the shape the backend emits as a scalar-base global access (base in
+// SGPRs, offset in one VGPR), with no 64-bit per-lane address arithmetic.
+template <typename T>
+__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void st_at(void* base, uint32_t byte_off, T x) {
+  *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off) = x;
+}
+__device__ __forceinline__ float ld_in_at(const float* base, uint32_t byte_off) {
+  return ld_at<float>(base, byte_off);
+}
+__device__ __forceinline__ float ld_in_at(const uint16_t* base, uint32_t byte_off) {
+  return bf16_bits_to_f32(ld_at<uint16_t>(base, byte_off));
+}
+__device__ __forceinline__ void st_out_at(float* base, uint32_t byte_off, float x) {
+  st_at<float>(base, byte_off, x);
+}
+__device__ __forceinline__ void st_out_at(uint16_t* base, uint32_t byte_off, float x) {
+  st_at<uint16_t>(base, byte_off, f32_to_bf16_bits(x));
+}
+
 template <typename T> __device__ __forceinline__ void store_out(T* p, size_t i, float x);
 template <> __device__ __forceinline__ void store_out<float>(float* p, size_t i, float x) { p[i] = x; }
 template <> __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, size_t i, float x) {

@@ -27,9 +27,9 @@
  *    (hipMalloc'd or equivalent). The library allocates nothing and keeps no
  *    global state; calls are re-entrant and may run on any stream.
  *  - Tensors are dense, row-major, packed (no strides). Alignment: q, k, g
- *    to 4 elements (16 bytes for fp32, 8 bytes for bf16); the forward's v,
- *    the workspace and the decode state S to 16 bytes; every other tensor to
- *    its element size.
+ *    to 4 elements (16 bytes for fp32, 8 bytes for bf16); the forward's v
+ *    and o, the workspace and the decode and speculative states S to 16
+ *    bytes; every other tensor to its element size.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
  *    All argument checks happen on the host before anything is launched; on
  *    any error nothing is launched and no output is written.

@@ -106,7 +106,8 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
     if (p.beta && !aligned(p.beta, es)) return KDA_ERR_ALIGNMENT;
   }
   if (pass) {
-    if ((p.v && !aligned(p.v, 16)) || (p.o && !aligned(p.o, eo))) return KDA_ERR_ALIGNMENT;
+    // v is read and o written as vectors (16-byte units, 8 bytes for bf16 o)
+    if ((p.v && !aligned(p.v, 16)) || (p.o && !aligned(p.o, 16))) return KDA_ERR_ALIGNMENT;
     if ((p.S0 && !aligned(p.S0, 4)) || (p.S_T && !aligned(p.S_T, 4))) return KDA_ERR_ALIGNMENT;
   }
   if (T > 0 && !aligned(p.ws, 16)) return KDA_ERR_ALIGNMENT;

@@ -365,13 +365,15 @@ struct ChunkFrags {
   }
 };
 
-// One chunk of the sequential pass on a dk x 16 state slice S (output layout):
-// U = Tb V - W S,  O = Qt S + M U,  S <- Diag(e^gamma) S + Kb^T U.  Returns O.
 // One chunk of the sequential pass on the fp16-operand path, with the
-// chunk's V rows 4gq + i (column c16) given in fp16.
-template <typename InT, int DK>
+// chunk's V rows 4gq + i (column c16) given in fp16. With kOT the output comes
+// back transposed: O^T = S^T Qt^T + U^T M^T is the same pair of products with
+// the operands swapped (each fragment already holds what the other operand
+// position needs), and it leaves lane (c16, gq) with token c16's value
+// columns 4gq .. 4gq+3, one contiguous vector store.
+template <bool kOT, typename InT, int DK>
 __device__ __forceinline__ f32x4 chunk_step_h(const ChunkFrags<InT, DK>& cur, f16x4 v16,
-                                            f32x4 (&S)[DK / 16]) {
+                                              f32x4 (&S)[DK / 16]) {
   constexpr int NM = DK / 16;
   f32x4 U, O;
   // Every accumulation chain below uses one MFMA shape (16x16x32). Two shapes
@@ -398,7 +400,8 @@ __device__ __forceinline__ f32x4 chunk_step_h(const ChunkFrags<InT, DK>& cur, f1
 #pragma unroll
   for (int p = 0; p < NM / 2; ++p) {
     U = mma_16x16x32_f16(cur.w[p], sh[p], U);                                // U = Ut - W S
-    O = mma_16x16x32_f16(cur.q[p], sh[p], O);                                // O = Qt S
+    O = kOT ? mma_16x16x32_f16(sh[p], cur.q[p], O)                           // O^T = S^T Qt^T
+            : mma_16x16x32_f16(cur.q[p], sh[p], O);                          // O = Qt S
   }
   f16x8 uu, mhl;
   f16x4 u4;
@@ -411,7 +414,8 @@ __device__ __forceinline__ f32x4 chunk_step_h(const ChunkFrags<InT, DK>& cur, f1
     mhl[i] = cur.mh[i];
     mhl[i + 4] = cur.ml[i];
   }
-  O = mma_16x16x32_f16(mhl, uu, O);                                          // O += (Mhi + Mlo) U
+  O = kOT ? mma_16x16x32_f16(uu, mhl, O)                                     // O^T += U^T M^T
+          : mma_16x16x32_f16(mhl, uu, O);                                    // O += (Mhi + Mlo) U
   // S = Diag(e^gamma) S + Kb^T U: the accumulator input is the VALU product
   // S * e^gamma, never another MFMA's output, so the 16x16x16 shape is safe.
 #pragma unroll
@@ -419,6 +423,8 @@ __device__ __forceinline__ f32x4 chunk_step_h(const ChunkFrags<InT, DK>& cur, f1
   return O;
 }
 
+// One chunk of the sequential pass on a dk x 16 state slice S (output layout):
+// U = Tb V - W S,  O = Qt S + M U,  S <- Diag(e^gamma) S + Kb^T U.  Returns O.
 template <typename InT, int DK>
 __device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<InT, DK>& cur, f32x4 (&S)[DK / 16]) {
   constexpr int NM = DK / 16;
@@ -447,7 +453,7 @@ __device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<InT, DK>& cur, f32x
     f16x4 v16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v16[i] = static_cast<_Float16>(cur.vv[i]);
-    O = chunk_step_h(cur, v16, S);
+    O = chunk_step_h<false>(cur, v16, S);
   }
   return O;
 }
@@ -604,8 +610,16 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
 // loads are issued kStages steps before they are written to LDS.
 // ---------------------------------------------------------------------------
 
-constexpr int kRing = 4;
-constexpr int kStages = 3;
+#ifndef KDA_RING_SLOTS
+#define KDA_RING_SLOTS 4
+#endif
+#ifndef KDA_RING_STAGES
+#define KDA_RING_STAGES 4
+#endif
+constexpr int kRing = KDA_RING_SLOTS;
+constexpr int kStages = KDA_RING_STAGES;
+static_assert(kRing >= 3, "the compute wave reads one slot ahead of the one it uses");
+
 
 // LDS-only release/acquire around a workgroup barrier: orders this wave's LDS
 // accesses against the other wave's, without waiting for global loads.
@@ -619,6 +633,12 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   __builtin_amdgcn_sched_barrier(0);
 }
+
+// 16-byte record loads per lane at dk = 128, plus one V load: the loads of
+// kStages - 1 chunks stay in flight at each commit, and that count must fit
+// the 6-bit load counter the waits encode.
+constexpr int kRingLoadsPerChunk = 14 + 1;
+static_assert((kStages - 1) * kRingLoadsPerChunk <= 63, "loads in flight exceed the wait counter");
 
 template <int DK>
 struct RingGeom {
@@ -663,7 +683,7 @@ __global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __res
   const size_t hb = static_cast<size_t>(b * T * H + h) * DV;
   const size_t chunk_elems = static_cast<size_t>(16 * H) * DV;
   const int64_t NF = T / 16;
-  const int64_t NC3 = (NC + 2) / 3 * 3;  // loader steps (and barriers), a multiple of 3
+  const int64_t NCS = (NC + kStages - 1) / kStages * kStages;  // loader steps (and barriers)
 
   if (wave == 0) {
     // ---------------- loader ----------------
@@ -705,32 +725,30 @@ __global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __res
         for (int i = 0; i < 4; ++i) vt[(cv + i) * 16 + tv] = static_cast<_Float16>(x[i]);
       }
     };
-    LoaderStage<DK> s0, s1, s2;
-    issue(s0, 0);
-    issue(s1, 1);
-    issue(s2, 2);
-    commit(s0, 0);
-    issue(s0, 3);
-    commit(s1, 1);
-    issue(s1, 4);
-    commit(s2, 2);
-    issue(s2, 5);
+    LoaderStage<DK> st[kStages];
+    // prologue: chunks 0 .. kStages-1 in flight, then slots 0 .. kRing-2
+    // filled (each commit refills its stage kStages chunks ahead)
+#pragma unroll
+    for (int c = 0; c < kStages; ++c) issue(st[c], c);
+#pragma unroll
+    for (int c = 0; c < kRing - 1; ++c) {
+      commit(st[c % kStages], c);
+      issue(st[c % kStages], c + kStages);
+    }
     ring_barrier();
-    // step n writes chunk n + 3 (slot (n - 1) % kRing) from stage n % 3 and
-    // refills that stage with chunk n + 6. The loop runs a multiple of 3
-    // steps with no exit in between (an exit inside would make the compiler
-    // drain every load at the loop's back edge); the compute wave pads its
-    // barriers to the same count.
-    for (int64_t n = 0; n < NC3; n += 3) {
-      commit(s0, n + 3);
-      issue(s0, n + 6);
-      ring_barrier();
-      commit(s1, n + 4);
-      issue(s1, n + 7);
-      ring_barrier();
-      commit(s2, n + 5);
-      issue(s2, n + 8);
-      ring_barrier();
+    // step n writes chunk n + kRing - 1 (slot (n - 1) % kRing) from its
+    // stage and refills that stage with the chunk kStages further on. The
+    // loop runs a multiple of kStages steps with no exit in between (an exit
+    // inside would make the compiler drain every load at the loop's back
+    // edge); the compute wave pads its barriers to the same count.
+    for (int64_t n = 0; n < NCS; n += kStages) {
+#pragma unroll
+      for (int k = 0; k < kStages; ++k) {
+        const int64_t c = n + k + kRing - 1;
+        commit(st[(k + kRing - 1) % kStages], c);
+        issue(st[(k + kRing - 1) % kStages], c + kStages);
+        ring_barrier();
+      }
     }
     return;
   }
@@ -745,20 +763,18 @@ __global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __res
     for (int i = 0; i < 4; ++i)
       S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
   OutT* ob = o + hb;
-  uint32_t obo[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    obo[i] = static_cast<uint32_t>((4 * gq + i) * H * DV + col) * static_cast<uint32_t>(sizeof(OutT));
+  // output in transposed fragments: lane (c16, gq) holds token c16, value
+  // columns slice*16 + 4gq .. +3 of the chunk
+  const uint32_t obt =
+      static_cast<uint32_t>(c16 * H * DV + slice * 16 + 4 * gq) * static_cast<uint32_t>(sizeof(OutT));
   int64_t next_snap = snap_chunks;
   float* snap_b = nullptr;
   if (snap_chunks > 0) {
     const int64_t ns = NF / snap_chunks;
     snap_b = snap + (static_cast<size_t>(b * ns) * H + h) * DK * DV + col;
   }
-  auto finish = [&](int64_t n, f32x4 O) __attribute__((always_inline)) {
-    OutT* oc = ob + static_cast<size_t>(n) * chunk_elems;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_out_at(oc, obo[i], O[i]);
+  auto finish = [&](int64_t n, f32x4 OT) __attribute__((always_inline)) {
+    st_out4_at(ob + static_cast<size_t>(n) * chunk_elems, obt, OT);
     if (n + 1 == next_snap) {
       float* sp = snap_b + static_cast<size_t>(n / snap_chunks) * H * DK * DV;
 #pragma unroll
@@ -782,36 +798,30 @@ __global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __res
   int64_t n = 0;
   for (; n + 1 < NF; n += 2) {
     read(f1, v1, n + 1);
-    finish(n, chunk_step_h(f0, v0, S));
+    finish(n, chunk_step_h<true>(f0, v0, S));
     ring_barrier();
     if (n + 2 < NC) read(f0, v0, n + 2);
-    finish(n + 1, chunk_step_h(f1, v1, S));
+    finish(n + 1, chunk_step_h<true>(f1, v1, S));
     ring_barrier();
   }
   if (n < NF) {  // an odd last full chunk, in f0
     if (n + 1 < NC) read(f1, v1, n + 1);
-    finish(n, chunk_step_h(f0, v0, S));
+    finish(n, chunk_step_h<true>(f0, v0, S));
     ring_barrier();
     ++n;
     if (NC > NF) {  // then the partial chunk, in f1
       const int valid = static_cast<int>(T - NF * 16);
-      const f32x4 O = chunk_step_h(f1, v1, S);
-      OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
+      const f32x4 OT = chunk_step_h<true>(f1, v1, S);
+      if (c16 < valid) st_out4_at(ob + static_cast<size_t>(NF) * chunk_elems, obt, OT);
       ring_barrier();
     }
   } else if (NC > NF) {  // even number of full chunks: the partial chunk is in f0
     const int valid = static_cast<int>(T - NF * 16);
-    const f32x4 O = chunk_step_h(f0, v0, S);
-    OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
+    const f32x4 OT = chunk_step_h<true>(f0, v0, S);
+    if (c16 < valid) st_out4_at(ob + static_cast<size_t>(NF) * chunk_elems, obt, OT);
     ring_barrier();
   }
-  for (int64_t k = NC; k < NC3; ++k) ring_barrier();  // match the loader's steps
+  for (int64_t k = NC; k < NCS; ++k) ring_barrier();  // match the loader's steps
   if (ST) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)

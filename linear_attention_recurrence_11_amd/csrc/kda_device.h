@@ -84,6 +84,20 @@ __device__ __forceinline__ void st_out_at(uint16_t* base, uint32_t byte_off, flo
   st_at<uint16_t>(base, byte_off, f32_to_bf16_bits(x));
 }
 
+// Four consecutive outputs at a uniform base plus a per-lane byte offset (16
+// bytes for fp32, 8 bytes of bf16 for bf16 outputs).
+__device__ __forceinline__ void st_out4_at(float* base, uint32_t byte_off, f32x4 x) {
+  st_at<f32x4>(base, byte_off, x);
+}
+__device__ __forceinline__ void st_out4_at(uint16_t* base, uint32_t byte_off, f32x4 x) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t w = {static_cast<uint32_t>(f32_to_bf16_bits(x[0])) |
+                         (static_cast<uint32_t>(f32_to_bf16_bits(x[1])) << 16),
+                     static_cast<uint32_t>(f32_to_bf16_bits(x[2])) |
+                         (static_cast<uint32_t>(f32_to_bf16_bits(x[3])) << 16)};
+  st_at<u32x2_t>(base, byte_off, w);
+}
+
 template <typename T> __device__ __forceinline__ void store_out(T* p, size_t i, float x);
 template <> __device__ __forceinline__ void store_out<float>(float* p, size_t i, float x) { p[i] = x; }
 template <> __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, size_t i, float x) {

@@ -105,7 +105,8 @@ def test_chunk_check_rejects(lib):
     assert check(lib, p, sz, ws=p["ws"] + 8) == ALIGN
     assert check(lib, p, sz, beta=p["beta"] + 2) == ALIGN
     assert check(lib, p, sz, beta=p["beta"] + 4) == OK      # element-aligned is enough
-    assert check(lib, p, sz, o=p["o"] + 4) == OK
+    assert check(lib, p, sz, o=p["o"] + 4) == ALIGN         # forward o: 16 bytes
+    assert check(lib, p, sz, o=p["o"] + 16) == OK
     assert check(lib, p, sz, o=p["q"]) == ALIAS            # o over q
     assert check(lib, p, sz, o=p["S0"]) == ALIAS           # o over S0
     assert check(lib, p, sz, S_T=p["S0"] + 64) == ALIAS    # partial state overlap

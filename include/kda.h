@@ -198,15 +198,16 @@ kda_status kda_decode_step_check(const void* q, const void* k, const void* v,
  *                   j = 0 .. T / snapshot_every - 1, with layout
  *                   [B, T / snapshot_every, H, dk, dv] fp32. snapshot_every
  *                   is 0 (none; snapshots ignored) or a positive multiple
- *                   of 16 (KDA_ERR_UNSUPPORTED otherwise; negative is
- *                   KDA_ERR_SHAPE); snapshots may be NULL only when no
+ *                   of 32, the state pass's step (KDA_ERR_UNSUPPORTED
+ *                   otherwise; negative is KDA_ERR_SHAPE); snapshots may be
+ *                   NULL only when no
  *                   snapshot falls inside T. They must not overlap any
  *                   other tensor or the workspace. 4-byte aligned.
  *
  * Snapshots serve a prefix cache that hashes fixed blocks of 512 tokens and
  * shares the recurrent state of a hit across requests ("177: Kimi K3 in
  * Detail", sections 10 and 16). Since chunks align at t = 0 and
- * snapshot_every is a multiple of 16, a later kda_chunk_fwd over the tokens
+ * snapshot_every is a multiple of 32, a later kda_chunk_fwd over the tokens
  * after snapshot j with S0 = snapshots[b, j] (for B = 1 that block is
  * exactly an [H, dk, dv] state) performs the same arithmetic as the
  * uninterrupted run: its o and S_T are bit-identical to the full run's.

@@ -13,6 +13,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
+# The argument lists below follow this version of include/kda.h.
+ABI_VERSION = 2
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_LOG_DECAY, KDA_GATE_SIGMOID = 0, 1
 _STATUS_OK = 0
@@ -40,6 +42,10 @@ def _load():
         vp, i64, i, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         lib.kda_abi_version.restype = i
         lib.kda_abi_version.argtypes = []
+        found = lib.kda_abi_version()
+        if found != ABI_VERSION:
+            raise RuntimeError("%s has ABI version %d, this binding expects %d; rebuild it"
+                               % (path, found, ABI_VERSION))
         lib.kda_status_str.restype = ctypes.c_char_p
         lib.kda_status_str.argtypes = [i]
         lib.kda_chunk_fwd_workspace_size.restype = sz

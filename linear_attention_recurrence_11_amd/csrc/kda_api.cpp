@@ -52,11 +52,12 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
   if (B < 0 || T < 0 || H < 0 || (dk != 64 && dk != 128) || !dtype_ok(in_dtype)) return 0;
   if (dv < 16 || dv > 512 || dv % 16 != 0) return 0;
   if (B > kMaxElems || T > kMaxElems || H > kMaxElems) return 0;
-  const int64_t NC = (T + 15) / 16;
-  const kda::RecordLayout L = kda::record_layout(dk, in_dtype == KDA_F32);
-  const double total = static_cast<double>(B) * H * NC * L.bytes;
+  // fp32 inputs: one record per 16-token chunk; bf16 inputs: one per pair
+  const int64_t units = in_dtype == KDA_F32 ? (T + 15) / 16 : (T + 31) / 32;
+  const int64_t bytes = in_dtype == KDA_F32 ? kda::record_layout(dk, true).bytes : kda::pair_layout(dk).bytes;
+  const double total = static_cast<double>(B) * H * units * bytes;
   if (total > 9.0e18) return 0;
-  return static_cast<size_t>(B * H * NC * L.bytes);
+  return static_cast<size_t>(B * H * units * bytes);
 }
 
 }  // extern "C"
@@ -130,7 +131,7 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
   if (overlap(rst, rs0) && p.S_T != p.S0) return KDA_ERR_ALIAS;
   // snapshots: [B, T / every, H, dk, dv] fp32 written by the pass stage
   if (p.snap_every < 0) return KDA_ERR_SHAPE;
-  if (p.snap_every % 16 != 0) return KDA_ERR_UNSUPPORTED;
+  if (p.snap_every % 32 != 0) return KDA_ERR_UNSUPPORTED;  // whole steps of the state pass
   const int64_t nsnap = p.snap_every > 0 ? T / p.snap_every : 0;
   if (pass && nsnap > 0) {
     if (!p.snaps) return KDA_ERR_NULL;

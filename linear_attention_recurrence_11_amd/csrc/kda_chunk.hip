@@ -298,6 +298,269 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// Pair prep (bf16 inputs): the record for two consecutive chunks c1 = 2s and
+// c2 = 2s + 1, so that the state pass can advance 32 tokens per step. With
+// S0 the state entering c1, S1 = Diag(e^g1) S0 + Kb1^T U1 the state entering
+// c2 (g1 = gamma of c1, per channel), the two chunks' lines become
+//   U1 = Ut1 - W1 S0
+//   U2 = Ut2 - W2 Diag(e^g1) S0 - C21 U1,          C21 = W2 Kb1^T
+//   O1 = Qt1 S0 + M1 U1
+//   O2 = Qt2 Diag(e^g1) S0 + M21 U1 + M2 U2,       M21 = Qt2 Kb1^T
+//   S2 = Diag(e^(g1 + g2)) S0 + [Diag(e^g2) Kb1^T | Kb2^T] [U1; U2]
+// (the off-diagonal 16-token tiles, C21 and M21, are dense products as well).
+// Every factor is a product of retentions, so nothing here exceeds 1 in size.
+// One wavefront per chunk (the per-chunk work is that of kda_chunk_prep);
+// wavefront 1 also forms C21 and M21 from wavefront 0's Kb1 through LDS.
+// ---------------------------------------------------------------------------
+
+template <int DK, int GATE>
+__global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ g,
+                                                           const uint16_t* __restrict__ beta,
+                                                           uint8_t* __restrict__ ws, int64_t T,
+                                                           int64_t H, int64_t NPR, PairLayout L) {
+  constexpr int NM = DK / 16;
+  constexpr int LDK = DK + 4;  // padded LDS row (conflict-free transposed reads)
+  using Op = _Float16;
+  __shared__ float s_beta[2][16];
+  __shared__ Op s_kt[2][16 * LDK];
+  __shared__ Op s_kb[2][16 * LDK];
+  __shared__ Op s_qt[16 * LDK];       // Qt of c2 (before the e^g1 factor)
+  __shared__ float s_eg[2][DK];       // e^gamma of each chunk, per channel
+  __shared__ float s_A[2][16][17];
+  __shared__ float s_T[2][16][17];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c16 = l & 15, gq = l >> 4;
+  const int64_t wg = blockIdx.x;  // ((b * NPR) + s) * H + h
+  const int64_t h = wg % H;
+  const int64_t bs = wg / H;
+  const int64_t sp = bs % NPR;
+  const int64_t b = bs / NPR;
+  const int64_t n = 2 * sp + w;  // this wavefront's chunk
+  const int64_t t = n * 16 + c16;
+  const bool valid = t < T;
+  const size_t tok = static_cast<size_t>((b * T + (valid ? t : 0)) * H + h);
+  uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NPR + sp) * L.bytes;
+
+  // ---- loads, kept packed until used ----
+  uint2 rq[NM], rk[NM], rg[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const size_t off = tok * DK + 16 * m + 4 * gq;
+    if (valid) {
+      rq[m] = *reinterpret_cast<const uint2*>(q + off);
+      rk[m] = *reinterpret_cast<const uint2*>(k + off);
+      rg[m] = *reinterpret_cast<const uint2*>(g + off);
+    } else {
+      rq[m] = rk[m] = rg[m] = uint2{};
+    }
+  }
+  if (gq == 0) s_beta[w][c16] = valid ? load_in(beta, tok) : 0.f;
+
+  // ---- per pair of 16-channel groups: decay scan, scaled operands, Gram ----
+  // (as in kda_chunk_prep; channel (m, i) = 16m + 4gq + i, Gram slot
+  // j = 4(m - 2p) + i)
+  f32x4 Araw = zero4(), MrawT = zero4();
+#pragma unroll
+  for (int p = 0; p < NM / 2; ++p) {
+    float qt[8], kt[8], kh[8];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int m = 2 * p + jj;
+      float xq[4], xk[4], xg[4];
+      unpack4(rq[m], xq);
+      unpack4(rk[m], xk);
+      unpack4(rg[m], xg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = (valid ? gate_decay<GATE>(xg[i]) : 0.f) * kLog2e;
+        const float G = row_inclusive_prefix_sum(x);
+        const float Gb = row_exclusive_suffix_sum(x);
+        const float E = __builtin_amdgcn_exp2f(G);
+        const float Eh = __builtin_amdgcn_exp2f(-G);
+        const float Eb = __builtin_amdgcn_exp2f(Gb);
+        const int j = 4 * jj + i;
+        const int ch = 16 * m + 4 * gq + i;
+        qt[j] = E * xq[i];
+        kt[j] = E * xk[i];
+        kh[j] = Eh * xk[i];
+        s_kt[w][c16 * LDK + ch] = static_cast<Op>(kt[j]);
+        s_kb[w][c16 * LDK + ch] = static_cast<Op>(Eb * xk[i]);
+        if (w == 1) s_qt[c16 * LDK + ch] = static_cast<Op>(qt[j]);
+        if (c16 == 15) s_eg[w][ch] = E;  // e^gamma: the decay to the chunk's end
+      }
+    }
+    bf16x8 kt_hi, kt_lo, kh_hi, kh_lo, qt_hi, qt_lo;
+    f16x8 qv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kt_hi[j] = static_cast<__bf16>(kt[j]);
+      kt_lo[j] = static_cast<__bf16>(kt[j] - static_cast<float>(kt_hi[j]));
+      kh_hi[j] = static_cast<__bf16>(kh[j]);
+      kh_lo[j] = static_cast<__bf16>(kh[j] - static_cast<float>(kh_hi[j]));
+      qt_hi[j] = static_cast<__bf16>(qt[j]);
+      qt_lo[j] = static_cast<__bf16>(qt[j] - static_cast<float>(qt_hi[j]));
+      qv[j] = static_cast<Op>(qt[j]);
+    }
+    Araw = mma_16x16x32_bf16(kt_hi, kh_hi, Araw);
+    Araw = mma_16x16x32_bf16(kt_hi, kh_lo, Araw);
+    Araw = mma_16x16x32_bf16(kt_lo, kh_hi, Araw);
+    MrawT = mma_16x16x32_bf16(kh_hi, qt_hi, MrawT);
+    MrawT = mma_16x16x32_bf16(kh_lo, qt_hi, MrawT);
+    MrawT = mma_16x16x32_bf16(kh_hi, qt_lo, MrawT);
+    if (w == 0) *reinterpret_cast<f16x8*>(rec + L.q1 + static_cast<size_t>(p * 64 + l) * 16) = qv;
+  }
+  __syncthreads();  // s_beta, s_kt, s_kb, s_qt, s_eg of both chunks visible
+
+  // ---- mask: A strictly lower with row scale beta_r ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * gq + i, c = c16;
+    s_A[w][r][c] = (c < r) ? s_beta[w][r] * Araw[i] : 0.f;
+  }
+  __syncthreads();
+
+  // ---- Tm = (I + A)^-1, column c16 per lane, by forward substitution ----
+  {
+    float tc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == c16) ? 1.f : 0.f;
+#pragma unroll
+      for (int c = 0; c < r; ++c) acc -= s_A[w][r][c] * tc[c];
+      tc[r] = acc;
+    }
+    if (gq == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_T[w][r][c16] = tc[r];
+    }
+  }
+  __syncthreads();
+
+  float tb[4], mf[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * gq + i;
+    tb[i] = s_T[w][c16][c] * s_beta[w][c];
+    mf[i] = (c <= c16) ? MrawT[i] : 0.f;
+  }
+
+  // ---- W^T tiles: lane gets W[c16][16m + 4gq + i] ----
+  float wv[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    f16x4 av, bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = s_kt[w][(4 * gq + i) * LDK + 16 * m + c16];
+      bv[i] = static_cast<_Float16>(tb[i]);
+    }
+    const f32x4 acc = mma_16x16x16_f16(av, bv, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[m][i] = acc[i];
+  }
+
+  const float* eg1 = s_eg[0];
+  const float* eg2 = s_eg[1];
+  if (w == 0) {
+    // ---- c1: -W1, [Kb1 e^g2 | .], [M1 hi | lo], Tb1 ----
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      f16x8 x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = static_cast<Op>(-wv[2 * p + (j >> 2)][j & 3]);
+      *reinterpret_cast<f16x8*>(rec + L.w1 + static_cast<size_t>(p * 64 + l) * 16) = x;
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const float e2 = eg2[16 * m + c16];
+      f16x4 kv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kv[i] = static_cast<Op>(static_cast<float>(s_kb[0][(4 * gq + i) * LDK + 16 * m + c16]) * e2);
+      *reinterpret_cast<f16x4*>(rec + L.kb + static_cast<size_t>(m * 64 + l) * 16) = kv;
+    }
+    f16x8 mm;
+    f16x4 tv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mm[i] = static_cast<Op>(mf[i]);
+      mm[i + 4] = static_cast<Op>(mf[i] - static_cast<float>(mm[i]));
+      tv[i] = static_cast<Op>(tb[i]);
+    }
+    *reinterpret_cast<f16x8*>(rec + L.m1 + static_cast<size_t>(l) * 16) = mm;
+    *reinterpret_cast<f16x4*>(rec + L.tb1 + static_cast<size_t>(l) * 8) = tv;
+  } else {
+    // ---- coupling tiles from Kb1 (wavefront 0's, in LDS): lane gets
+    // C21[c16][4gq + i] and M21[c16][4gq + i] (products with Kb1 as the
+    // first operand come out transposed) ----
+    f32x4 C21T = zero4(), M21T = zero4();
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      f16x8 kb1, w2, q2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = 2 * p + (j >> 2), i = j & 3;
+        const int ch = 16 * m + 4 * gq + i;
+        kb1[j] = s_kb[0][c16 * LDK + ch];
+        w2[j] = static_cast<Op>(wv[m][i]);
+        q2[j] = s_qt[c16 * LDK + ch];
+      }
+      C21T = mma_16x16x32_f16(kb1, w2, C21T);
+      M21T = mma_16x16x32_f16(kb1, q2, M21T);
+    }
+    // ---- c2: -W2 e^g1, Qt2 e^g1, [. | Kb2], [M21 | M2] hi and lo,
+    // [Tb2 | -C21], e^(g1 + g2) ----
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      f16x8 x, y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int m = 2 * p + (j >> 2), i = j & 3;
+        const int ch = 16 * m + 4 * gq + i;
+        const float e1 = eg1[ch];
+        x[j] = static_cast<Op>(-wv[m][i] * e1);
+        y[j] = static_cast<Op>(static_cast<float>(s_qt[c16 * LDK + ch]) * e1);
+      }
+      *reinterpret_cast<f16x8*>(rec + L.w2 + static_cast<size_t>(p * 64 + l) * 16) = x;
+      *reinterpret_cast<f16x8*>(rec + L.q2 + static_cast<size_t>(p * 64 + l) * 16) = y;
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      f16x4 kv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[i] = s_kb[1][(4 * gq + i) * LDK + 16 * m + c16];
+      *reinterpret_cast<f16x4*>(rec + L.kb + static_cast<size_t>(m * 64 + l) * 16 + 8) = kv;
+    }
+    f16x8 mh, ml, tc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Op a = static_cast<Op>(M21T[i]), c = static_cast<Op>(mf[i]);
+      mh[i] = a;
+      ml[i] = static_cast<Op>(M21T[i] - static_cast<float>(a));
+      mh[i + 4] = c;
+      ml[i + 4] = static_cast<Op>(mf[i] - static_cast<float>(c));
+      tc[i] = static_cast<Op>(tb[i]);
+      tc[i + 4] = static_cast<Op>(-C21T[i]);
+    }
+    *reinterpret_cast<f16x8*>(rec + L.m2h + static_cast<size_t>(l) * 16) = mh;
+    *reinterpret_cast<f16x8*>(rec + L.m2l + static_cast<size_t>(l) * 16) = ml;
+    *reinterpret_cast<f16x8*>(rec + L.tc2 + static_cast<size_t>(l) * 16) = tc;
+    if (c16 == 15) {  // e^(gamma1 + gamma2), laid out as eg of kda_chunk_prep
+      float* egp = reinterpret_cast<float*>(rec + L.eg) + gq * (DK / 4);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = eg1[16 * m + 4 * gq + i] * eg2[16 * m + 4 * gq + i];
+        *reinterpret_cast<float4*>(egp + 4 * m) = make_float4(e[0], e[1], e[2], e[3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Sequential state pass.
 // ---------------------------------------------------------------------------
 
@@ -590,44 +853,46 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
 }
 
 // ---------------------------------------------------------------------------
-// Sequential state pass, fp16-operand path: a loader wave and a compute wave.
+// Sequential state pass, bf16 inputs: two loader wavefronts and a compute
+// wavefront per (b, h, 16-column slice), advancing 32 tokens per step.
 //
-// The sequential chain (U = Ut - W S, S <- Diag(e^gamma) S + Kb^T U) runs on
-// one wavefront per (b, h, 16-column slice). Fed from global memory directly,
-// that wavefront waits on its own prefetch loads: the compiler's wait
-// placement in an unrolled prefetch loop leaves only about one chunk of
-// loads in flight, and HBM latency then sets the pace. Here a second
-// wavefront of the same workgroup streams each chunk's record and V tile
-// from HBM into a ring of LDS slots, several chunks ahead, with coalesced
-// 16-byte loads (and converts V to fp16, transposed for the MFMA operand);
-// the compute wavefront only reads LDS. One LDS-only barrier per chunk keeps
-// the two in step. Barrier 0 follows the loader's prologue, barrier n + 1
-// ends the compute wave's step n:
-//   prologue         the loader fills slots 0 .. kRing-2 with chunks
-//                    0 .. kRing-2;
-//   compute step n   uses chunk n (read into registers during step n - 1)
-//                    and reads chunk n + 1 from its slot;
-//   loader step n    between barriers n and n + 1, writes chunk n + kRing - 1
-//                    into slot (n - 1) % kRing, whose previous chunk the
-//                    compute wave finished reading before barrier n - 1;
-//                    the write is complete at barrier n + 1, and the chunk is
-//                    read after barrier n + kRing - 3 >= n + 1.
-// The loader keeps kStages chunks of loads in registers, so each chunk's
-// loads are issued kStages steps before they are written to LDS. Measured
-// settings: kStages = 4 with kRing = 4 (2 stages: 2.06 ms; 6 slots slower;
-// taking the barrier before the LDS writes instead of after: 3% slower).
+// The compute wavefront keeps its dk x 16 slice of S in registers and runs
+// the sequential chain. Fed from global memory directly, a wavefront waits on
+// its own prefetch loads (the compiler's wait placement in an unrolled
+// prefetch loop leaves about one step of loads in flight, and HBM latency
+// then sets the pace). Here the loader wavefronts stream each pair record and
+// its V tiles from HBM into a ring of LDS slots, several steps ahead, with
+// coalesced 16-byte loads (converting V to fp16, transposed for the MFMA
+// operand); the compute wavefront only reads LDS. One LDS-only barrier per
+// step keeps the three in step. Barrier 0 follows the loader's prologue,
+// barrier n + 1 ends step n:
+//   prologue         the loader fills slots 0 .. kSlots-2 with pairs
+//                    0 .. kSlots-2;
+//   compute step n   reads pair n from its slot and processes it;
+//   loader step n    between barriers n and n + 1, writes pair n + kSlots - 1
+//                    into the slot of pair n - 1, which the compute wave read
+//                    before barrier n; the write is complete at barrier n + 1,
+//                    before its pair is read (after barrier n + kSlots - 1).
+// Each loader keeps kStages pairs of its share of the loads in registers, so
+// each pair's loads are issued kStages steps before they are written to LDS.
+// Its loop runs a multiple of kStages steps with no exit in between (an exit
+// inside made the compiler drain every load at the loop's back edge); the
+// compute wave pads its barrier count to match.
+//
+// Per step the compute wavefront evaluates the pair lines of
+// kda_chunk_prep_pair: 29 16x16x32 MFMAs, one decay multiply and one fp16
+// conversion of its state slice, two output stores and one barrier, against
+// 36 MFMAs and two of each of the rest for two 16-token steps.
 // ---------------------------------------------------------------------------
 
-constexpr int kRing = 4;
-constexpr int kStages = 4;
-static_assert(kRing >= 3, "the compute wave reads one slot ahead of the one it uses");
-
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // LDS-only release/acquire around a workgroup barrier: orders this wave's LDS
-// accesses against the other wave's, without waiting for global loads.
-// The scheduling barriers keep the instruction scheduler from moving work
-// across steps (it would otherwise hoist the loader's use of loaded data to
-// the top of the loop, where it must wait for every load in flight).
+// accesses against the other wave's, without waiting for global loads. The
+// scheduling barriers keep the instruction scheduler from moving work across
+// steps (it would otherwise hoist the loader's use of loaded data to the top
+// of the loop, where it must wait for every load in flight).
 __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -636,42 +901,83 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// 16-byte record loads per lane at dk = 128, plus one V load: the loads of
-// kStages - 1 chunks stay in flight at each commit, and that count must fit
-// the 6-bit load counter the waits encode.
-constexpr int kRingLoadsPerChunk = 14 + 1;
-static_assert((kStages - 1) * kRingLoadsPerChunk <= 63, "loads in flight exceed the wait counter");
-
 template <int DK>
-struct RingGeom {
-  static constexpr int kRec = DK == 128 ? 14336 : 8192;  // record bytes (bf16 inputs)
-  static constexpr int kUnits = kRec / 1024;             // 16-byte loads per lane
-  static constexpr int kSlot = kRec + 512;               // + V^T tile, 16x16 fp16
+struct Ring32Geom {
+  static constexpr int kRec = DK == 128 ? 29696 : 17408;  // pair record bytes (pair_layout)
+  static constexpr int kUnits = kRec / 1024;              // 16-byte record loads per lane
+  static constexpr int kSlot = kRec + 1024;               // + two V^T tiles, 16x16 fp16
+  // Four slots let the loaders run up to three pairs ahead of the compute
+  // wave, which absorbs the jitter of either side (measured on the 64K-token
+  // workload: 3 slots 1.48-1.51 ms, 4 slots 1.46-1.48, 5 slots 1.50).
+  static constexpr int kSlots = 4;
+  // loader wavefronts: loader w loads record units j = w, w + kLoaders, ...;
+  // the last one also loads V. Each has its own load counter, so each can
+  // keep more pairs in flight: kStages - 1 pairs of its loads stay
+  // outstanding at each commit, within the 6-bit wait counter (one loader
+  // 1.51 ms, two 1.48, three 1.52).
+  static constexpr int kLoaders = 2;
+  static constexpr int kUnitsPer = (kUnits + kLoaders - 1) / kLoaders;
+  static constexpr int kStagesRaw = 1 + 63 / (kUnitsPer + 1);
+  static constexpr int kStages = kStagesRaw > 5 ? 5 : kStagesRaw;
+  static_assert((kStages - 1) * (kUnitsPer + 1) <= 63, "loads in flight exceed the wait counter");
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int DK>
+struct Loader32Stage {
+  u32x4 r[Ring32Geom<DK>::kUnitsPer];
+  u32x4 v;
+  bool v_ok;
+};
 
 template <int DK>
-struct LoaderStage {
-  u32x4 r[RingGeom<DK>::kUnits];
-  u32x2 v;
-  bool v_ok;  // the V token exists (applied at commit: a select right after
-              // the load would make the compiler wait for it there)
+struct PairFrags {
+  static constexpr int NM = DK / 16;
+  f16x8 w1[NM / 2], w2[NM / 2], q1[NM / 2], q2[NM / 2];
+  f16x8 kb[NM];
+  f16x8 m1, m2h, m2l, tc2;
+  f16x4 tb1, v1, v2;
+  f32x4 eg[NM];
+
+  __device__ __forceinline__ void load(const uint8_t* slot, const PairLayout& L, int l, int gq, int c16) {
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      const uint32_t off = static_cast<uint32_t>(p * 64 + l) * 16;
+      w1[p] = ld_at<f16x8>(slot + L.w1, off);
+      w2[p] = ld_at<f16x8>(slot + L.w2, off);
+      q1[p] = ld_at<f16x8>(slot + L.q1, off);
+      q2[p] = ld_at<f16x8>(slot + L.q2, off);
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      kb[m] = ld_at<f16x8>(slot + L.kb, static_cast<uint32_t>(m * 64 + l) * 16);
+      eg[m] = ld_at<f32x4>(slot + L.eg, static_cast<uint32_t>(gq * NM + m) * 16);
+    }
+    const uint32_t lo = static_cast<uint32_t>(l) * 16;
+    m1 = ld_at<f16x8>(slot + L.m1, lo);
+    m2h = ld_at<f16x8>(slot + L.m2h, lo);
+    m2l = ld_at<f16x8>(slot + L.m2l, lo);
+    tc2 = ld_at<f16x8>(slot + L.tc2, lo);
+    tb1 = ld_at<f16x4>(slot + L.tb1, static_cast<uint32_t>(l) * 8);
+    const uint8_t* vt = slot + Ring32Geom<DK>::kRec;
+    const uint32_t vo = static_cast<uint32_t>(c16 * 16 + 4 * gq) * 2;
+    v1 = ld_at<f16x4>(vt, vo);
+    v2 = ld_at<f16x4>(vt + 512, vo);
+  }
 };
 
 template <typename OutT, int DK>
-__global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __restrict__ v,
-                                                           const uint8_t* __restrict__ ws,
-                                                           const float* S0, OutT* __restrict__ o,
-                                                           float* ST, float* __restrict__ snap,
-                                                           int64_t snap_chunks, int64_t T, int64_t H,
-                                                           int64_t DV, int64_t NC, int64_t nslices,
-                                                           int64_t nheads, RecordLayout L) {
-  using G = RingGeom<DK>;
+__global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state_pass_ring32(const uint16_t* __restrict__ v,
+                                                             const uint8_t* __restrict__ ws,
+                                                             const float* S0, OutT* __restrict__ o,
+                                                             float* ST, float* __restrict__ snap,
+                                                             int64_t snap_pairs, int64_t T,
+                                                             int64_t H, int64_t DV, int64_t NPR,
+                                                             int64_t nslices, int64_t nheads,
+                                                             PairLayout L) {
+  using G = Ring32Geom<DK>;
   constexpr int NM = DK / 16;
-  using Frags = ChunkFrags<uint16_t, DK>;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * G::kSlot];
+  constexpr int kR = G::kSlots, kS = G::kStages;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kR * G::kSlot];
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, c16 = l & 15, gq = l >> 4;
   // XCD-aware numbering, as in kda_state_pass.
@@ -681,74 +987,77 @@ __global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __res
   const int64_t slice = kk % nslices;
   if (head >= nheads) return;  // whole workgroup
   const int64_t b = head / H, h = head % H;
-  const uint8_t* rec0 = ws + static_cast<size_t>(head) * NC * G::kRec;
+  const uint8_t* rec0 = ws + static_cast<size_t>(head) * NPR * G::kRec;
   const size_t hb = static_cast<size_t>(b * T * H + h) * DV;
-  const size_t chunk_elems = static_cast<size_t>(16 * H) * DV;
-  const int64_t NF = T / 16;
-  const int64_t NCS = (NC + kStages - 1) / kStages * kStages;  // loader steps (and barriers)
+  const size_t pair_elems = static_cast<size_t>(32 * H) * DV;  // v or o elements per 32 tokens
+  const int64_t NPF = T / 32;                                  // full pairs
+  const int64_t NPS = (NPR + kS - 1) / kS * kS;                // loader steps (and barriers)
 
-  if (wave == 0) {
-    // ---------------- loader ----------------
-    // V: lane -> token tv of the chunk, columns cv .. cv+3 of the slice.
-    const int tv = l >> 2, cv = 4 * (l & 3);
+  constexpr int kLd = G::kLoaders;
+  if (wave < kLd) {
+    // ---------------- loaders ----------------
+    const bool has_v = wave == kLd - 1;
+    // V: lane -> token tv of the pair (0..31), columns cv .. cv+7 of the slice
+    const int tv = l >> 1, cv = 8 * (l & 1);
     const uint32_t vcol = static_cast<uint32_t>(slice * 16 + cv);
     const uint32_t vrow = static_cast<uint32_t>(H * DV);  // elements per token
     const uint16_t* vb = v + hb;
-    // Loads are unconditional (chunks past the end re-read the last one, V
-    // tokens past T are zeroed by a select): a branch around them would make
-    // the compiler's wait counting conservative at the join.
-    auto issue = [&](LoaderStage<DK>& st, int64_t c) __attribute__((always_inline)) {
-      const int64_t cc = c < NC ? c : NC - 1;
+    // Loads are unconditional (pairs past the end re-read the last one; V
+    // tokens past T read the last token and are zeroed at commit): a branch
+    // around them would make the compiler's wait counting conservative.
+    auto issue = [&](Loader32Stage<DK>& st, int64_t c) __attribute__((always_inline)) {
+      const int64_t cc = c < NPR ? c : NPR - 1;
       const uint8_t* src = rec0 + static_cast<size_t>(cc) * G::kRec;
 #pragma unroll
-      for (int j = 0; j < G::kUnits; ++j) st.r[j] = ld_at<u32x4>(src, static_cast<uint32_t>(j * 64 + l) * 16);
-      // tokens past T (last partial chunk) read the last token instead: every
-      // load stays inside v; the value is zeroed at commit
-      const int64_t tmax = T - 1 - cc * 16;
-      const uint32_t t = static_cast<uint32_t>(tv < tmax ? tv : tmax);
-      st.v = ld_at<u32x2>(vb + static_cast<size_t>(cc) * chunk_elems, (t * vrow + vcol) * 2u);
-      st.v_ok = c * 16 + tv < T;
-    };
-    // Commits are unconditional too: a chunk past the end lands in a slot
-    // the compute wave reads no more (the same reuse distance as in the
-    // steady state), and is never read.
-    auto commit = [&](const LoaderStage<DK>& st, int64_t c) __attribute__((always_inline)) {
-      {
-        uint8_t* dst = ring + static_cast<int>(c % kRing) * G::kSlot;
-#pragma unroll
-        for (int j = 0; j < G::kUnits; ++j) st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[j]);
-        // V^T[col][token] in fp16: the compute lane (c16, gq) reads the four
-        // tokens 4gq .. 4gq+3 of column c16 as one 8-byte word.
-        const uint32_t v0 = st.v_ok ? st.v[0] : 0u, v1 = st.v_ok ? st.v[1] : 0u;
-        const float x[4] = {__uint_as_float(v0 << 16), __uint_as_float(v0 & 0xffff0000u),
-                            __uint_as_float(v1 << 16), __uint_as_float(v1 & 0xffff0000u)};
-        _Float16* vt = reinterpret_cast<_Float16*>(dst + G::kRec);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vt[(cv + i) * 16 + tv] = static_cast<_Float16>(x[i]);
+      for (int u = 0; u < G::kUnitsPer; ++u) {
+        const int j = wave + u * kLd;
+        if (j < G::kUnits) st.r[u] = ld_at<u32x4>(src, static_cast<uint32_t>(j * 64 + l) * 16);
+      }
+      if (has_v) {
+        const int64_t tmax = T - 1 - cc * 32;
+        const uint32_t tt = static_cast<uint32_t>(tv < tmax ? tv : tmax);
+        st.v = ld_at<u32x4>(vb + static_cast<size_t>(cc) * pair_elems, (tt * vrow + vcol) * 2u);
+        st.v_ok = c * 32 + tv < T;
       }
     };
-    LoaderStage<DK> st[kStages];
-    // prologue: chunks 0 .. kStages-1 in flight, then slots 0 .. kRing-2
-    // filled (each commit refills its stage kStages chunks ahead)
+    // Commits are unconditional too: a pair past the end lands in a slot the
+    // compute wave reads no more, and is never read.
+    auto commit = [&](const Loader32Stage<DK>& st, int64_t c) __attribute__((always_inline)) {
+      uint8_t* dst = ring + static_cast<int>(c % kR) * G::kSlot;
 #pragma unroll
-    for (int c = 0; c < kStages; ++c) issue(st[c], c);
+      for (int u = 0; u < G::kUnitsPer; ++u) {
+        const int j = wave + u * kLd;
+        if (j < G::kUnits) st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[u]);
+      }
+      if (has_v) {
+        // V^T[col][token] in fp16, one 16x16 tile per chunk of the pair: the
+        // compute lane (c16, gq) reads tokens 4gq .. 4gq+3 of column c16.
+        _Float16* vt = reinterpret_cast<_Float16*>(dst + G::kRec) + (tv >> 4) * 256 + (tv & 15);
 #pragma unroll
-    for (int c = 0; c < kRing - 1; ++c) {
-      commit(st[c % kStages], c);
-      issue(st[c % kStages], c + kStages);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = st.v_ok ? st.v[i] : 0u;
+          vt[(cv + 2 * i) * 16] = static_cast<_Float16>(__uint_as_float(x << 16));
+          vt[(cv + 2 * i + 1) * 16] = static_cast<_Float16>(__uint_as_float(x & 0xffff0000u));
+        }
+      }
+    };
+    Loader32Stage<DK> st[kS];
+#pragma unroll
+    for (int c = 0; c < kS; ++c) issue(st[c], c);
+#pragma unroll
+    for (int c = 0; c < kR - 1; ++c) {
+      commit(st[c % kS], c);
+      issue(st[c % kS], c + kS);
     }
     ring_barrier();
-    // step n writes chunk n + kRing - 1 (slot (n - 1) % kRing) from its
-    // stage and refills that stage with the chunk kStages further on. The
-    // loop runs a multiple of kStages steps with no exit in between (an exit
-    // inside would make the compiler drain every load at the loop's back
-    // edge); the compute wave pads its barriers to the same count.
-    for (int64_t n = 0; n < NCS; n += kStages) {
+    // step n writes pair n + kR - 1 and refills its stage kS pairs ahead; a
+    // multiple of kS steps with no exit in between
+    for (int64_t n = 0; n < NPS; n += kS) {
 #pragma unroll
-      for (int k = 0; k < kStages; ++k) {
-        const int64_t c = n + k + kRing - 1;
-        commit(st[(k + kRing - 1) % kStages], c);
-        issue(st[(k + kRing - 1) % kStages], c + kStages);
+      for (int k = 0; k < kS; ++k) {
+        const int64_t c = n + k + kR - 1;
+        commit(st[(k + kR - 1) % kS], c);
+        issue(st[(k + kR - 1) % kS], c + kS);
         ring_barrier();
       }
     }
@@ -765,65 +1074,82 @@ __global__ __launch_bounds__(128) void kda_state_pass_ring(const uint16_t* __res
     for (int i = 0; i < 4; ++i)
       S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
   OutT* ob = o + hb;
-  // output in transposed fragments: lane (c16, gq) holds token c16, value
-  // columns slice*16 + 4gq .. +3 of the chunk
+  // outputs in transposed fragments: lane (c16, gq) holds token c16 of the
+  // chunk, value columns slice*16 + 4gq .. +3
   const uint32_t obt =
       static_cast<uint32_t>(c16 * H * DV + slice * 16 + 4 * gq) * static_cast<uint32_t>(sizeof(OutT));
-  int64_t next_snap = snap_chunks;
+  const size_t chunk_elems = pair_elems / 2;
+  int64_t next_snap = snap_pairs;
   float* snap_b = nullptr;
-  if (snap_chunks > 0) {
-    const int64_t ns = NF / snap_chunks;
+  if (snap_pairs > 0) {
+    const int64_t ns = NPF / snap_pairs;
     snap_b = snap + (static_cast<size_t>(b * ns) * H + h) * DK * DV + col;
   }
-  auto finish = [&](int64_t n, f32x4 OT) __attribute__((always_inline)) {
-    st_out4_at(ob + static_cast<size_t>(n) * chunk_elems, obt, OT);
-    if (n + 1 == next_snap) {
-      float* sp = snap_b + static_cast<size_t>(n / snap_chunks) * H * DK * DV;
+  ring_barrier();
+  for (int64_t n = 0; n < NPR; ++n) {
+    PairFrags<DK> f;
+    f.load(ring + static_cast<int>(n % kR) * G::kSlot, L, l, gq, c16);
+    f16x8 sh[NM / 2];
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
+    f16x8 tbz, vz;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tbz[i] = f.tb1[i];
+      tbz[i + 4] = static_cast<_Float16>(0.f);
+      vz[i] = f.v1[i];
+      vz[i + 4] = static_cast<_Float16>(0.f);
+    }
+    f32x4 U1 = mma_16x16x32_f16(tbz, vz, zero4());               // Tb1 V1
+    f32x4 U2 = zero4(), O1 = zero4(), O2 = zero4();
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      U1 = mma_16x16x32_f16(f.w1[p], sh[p], U1);                  // - W1 S0
+      U2 = mma_16x16x32_f16(f.w2[p], sh[p], U2);                  // - W2 e^g1 S0
+      O1 = mma_16x16x32_f16(sh[p], f.q1[p], O1);                  // (Qt1 S0)^T
+      O2 = mma_16x16x32_f16(sh[p], f.q2[p], O2);                  // (Qt2 e^g1 S0)^T
+    }
+    f16x8 u11, vu, u12;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 x = static_cast<_Float16>(U1[i]);
+      u11[i] = x;
+      u11[i + 4] = x;
+      vu[i] = f.v2[i];
+      vu[i + 4] = x;
+      u12[i] = x;
+    }
+    U2 = mma_16x16x32_f16(f.tc2, vu, U2);                         // + Tb2 V2 - C21 U1
+    O1 = mma_16x16x32_f16(u11, f.m1, O1);                         // + (M1 U1)^T
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u12[i + 4] = static_cast<_Float16>(U2[i]);
+    O2 = mma_16x16x32_f16(u12, f.m2h, O2);                        // + ([M21 | M2] [U1; U2])^T
+    O2 = mma_16x16x32_f16(u12, f.m2l, O2);
+    // S = Diag(e^(g1+g2)) S + [Kb1 e^g2 | Kb2]^T [U1; U2] (accumulator input
+    // is the VALU product)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) S[m] = mma_16x16x32_f16(f.kb[m], u12, S[m] * f.eg[m]);
+    OutT* oc = ob + static_cast<size_t>(n) * pair_elems;
+    if (n < NPF) {
+      st_out4_at(oc, obt, O1);
+      st_out4_at(oc + chunk_elems, obt, O2);
+    } else {  // last, partial pair: tokens past T are not stored
+      if (n * 32 + c16 < T) st_out4_at(oc, obt, O1);
+      if (n * 32 + 16 + c16 < T) st_out4_at(oc + chunk_elems, obt, O2);
+    }
+    if (n + 1 == next_snap && n < NPF) {
+      float* sp = snap_b + static_cast<size_t>(n / snap_pairs) * H * DK * DV;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sp[static_cast<size_t>(16 * m + 4 * gq + i) * DV] = S[m][i];
-      next_snap += snap_chunks;
+      next_snap += snap_pairs;
     }
-  };
-  auto read = [&](Frags& f, f16x4& vh, int64_t c) __attribute__((always_inline)) {
-    const uint8_t* src = ring + static_cast<int>(c % kRing) * G::kSlot;
-    f.load_record(src, L, l, gq);
-    vh = ld_at<f16x4>(src + G::kRec, static_cast<uint32_t>(c16 * 16 + 4 * gq) * 2);
-  };
-  ring_barrier();
-  Frags f0, f1;
-  f16x4 v0, v1;
-  read(f0, v0, 0);
-  // Full chunks, two per iteration (the fragment buffers alternate by
-  // position, never by copy); the next chunk's slot is read one step ahead.
-  int64_t n = 0;
-  for (; n + 1 < NF; n += 2) {
-    read(f1, v1, n + 1);
-    finish(n, chunk_step_h<true>(f0, v0, S));
-    ring_barrier();
-    if (n + 2 < NC) read(f0, v0, n + 2);
-    finish(n + 1, chunk_step_h<true>(f1, v1, S));
     ring_barrier();
   }
-  if (n < NF) {  // an odd last full chunk, in f0
-    if (n + 1 < NC) read(f1, v1, n + 1);
-    finish(n, chunk_step_h<true>(f0, v0, S));
-    ring_barrier();
-    ++n;
-    if (NC > NF) {  // then the partial chunk, in f1
-      const int valid = static_cast<int>(T - NF * 16);
-      const f32x4 OT = chunk_step_h<true>(f1, v1, S);
-      if (c16 < valid) st_out4_at(ob + static_cast<size_t>(NF) * chunk_elems, obt, OT);
-      ring_barrier();
-    }
-  } else if (NC > NF) {  // even number of full chunks: the partial chunk is in f0
-    const int valid = static_cast<int>(T - NF * 16);
-    const f32x4 OT = chunk_step_h<true>(f0, v0, S);
-    if (c16 < valid) st_out4_at(ob + static_cast<size_t>(NF) * chunk_elems, obt, OT);
-    ring_barrier();
-  }
-  for (int64_t k = NC; k < NCS; ++k) ring_barrier();  // match the loader's steps
+  for (int64_t k = NPR; k < NPS; ++k) ring_barrier();  // match the loader's steps
   if (ST) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -840,14 +1166,28 @@ __global__ void kda_copy_state(const float* S0, float* ST, int64_t n) {
 
 template <typename InT, int DK, int GATE>
 hipError_t launch_prep_typed(const ChunkFwdArgs& a, hipStream_t stream) {
-  const RecordLayout L = record_layout(DK, Path<InT>::kF32);
-  const int64_t NC = (a.T + 15) / 16;
-  const int64_t blocks = a.B * NC * a.H;
-  hipLaunchKernelGGL((kda_chunk_prep<InT, DK, GATE>), dim3(static_cast<uint32_t>(blocks)), dim3(64), 0,
-                     stream, static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
-                     static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta),
-                     static_cast<uint8_t*>(a.workspace), a.T, a.H, NC, L);
-  return hipGetLastError();
+  if constexpr (!Path<InT>::kF32) {  // bf16 inputs: one record per pair of chunks
+    const PairLayout L = pair_layout(DK);
+    if (L.bytes != Ring32Geom<DK>::kRec) return hipErrorInvalidValue;
+    const int64_t NPR = (a.T + 31) / 32;
+    const int64_t blocks = a.B * NPR * a.H;
+    hipLaunchKernelGGL((kda_chunk_prep_pair<DK, GATE>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(128), 0, stream, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.g),
+                       static_cast<const uint16_t*>(a.beta), static_cast<uint8_t*>(a.workspace),
+                       a.T, a.H, NPR, L);
+    return hipGetLastError();
+  } else {
+    const RecordLayout L = record_layout(DK, true);
+    const int64_t NC = (a.T + 15) / 16;
+    const int64_t blocks = a.B * NC * a.H;
+    hipLaunchKernelGGL((kda_chunk_prep<InT, DK, GATE>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64), 0, stream, static_cast<const InT*>(a.q),
+                       static_cast<const InT*>(a.k), static_cast<const InT*>(a.g),
+                       static_cast<const InT*>(a.beta), static_cast<uint8_t*>(a.workspace), a.T,
+                       a.H, NC, L);
+    return hipGetLastError();
+  }
 }
 
 // Snapshots are taken only when at least one falls inside the sequence.
@@ -863,21 +1203,25 @@ hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   const int64_t nheads = a.B * a.H;
   const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
   const int64_t snap_chunks = wants_snapshots(a) ? a.snapshot_every / 16 : 0;
-  if constexpr (!Path<InT>::kF32) {
-    if (L.bytes != RingGeom<DK>::kRec) return hipErrorInvalidValue;  // layout and ring disagree
-    hipLaunchKernelGGL((kda_state_pass_ring<OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(128), 0, stream, static_cast<const uint16_t*>(a.v),
+  if constexpr (!Path<InT>::kF32) {  // bf16 inputs: 32 tokens per step
+    const PairLayout P = pair_layout(DK);
+    if (P.bytes != Ring32Geom<DK>::kRec) return hipErrorInvalidValue;  // layout and ring disagree
+    const int64_t NPR = (a.T + 31) / 32;
+    const int64_t snap_pairs = snap_chunks / 2;
+    hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64 * (Ring32Geom<DK>::kLoaders + 1)), 0, stream, static_cast<const uint16_t*>(a.v),
+                       static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
+                       a.S_T, snap_pairs > 0 ? a.snapshots : nullptr, snap_pairs, a.T, a.H, a.dv,
+                       NPR, nslices, nheads, P);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64), 0, stream, static_cast<const InT*>(a.v),
                        static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
                        a.S_T, snap_chunks > 0 ? a.snapshots : nullptr, snap_chunks, a.T, a.H, a.dv,
                        NC, nslices, nheads, L);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(64), 0, stream, static_cast<const InT*>(a.v),
-                     static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
-                     a.S_T, snap_chunks > 0 ? a.snapshots : nullptr, snap_chunks, a.T, a.H, a.dv, NC,
-                     nslices, nheads, L);
-  return hipGetLastError();
 }
 
 template <typename InT, int DK>

@@ -37,17 +37,19 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.kda_abi_version() == 2
+    assert binding.kda_abi_version() == binding.ABI_VERSION == 2
     for s in range(8):
         assert binding.kda_status_str(s) and binding.kda_status_str(s) != "unknown status"
     assert binding.kda_status_str(99) == "unknown status"
 
 
 def test_workspace_size(lib):
-    # 16-token chunks; one record per (b, h, chunk), whole KiB: 14336 B (bf16 in,
-    # dk 128), 27648 B (fp32 in, dk 128), 15360 B (fp32 in, dk 64)
-    assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == 32 * 4096 * 14336
-    assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == 64 * 256 * 14336
+    # fp32 inputs: one record per (b, h, 16-token chunk), whole KiB: 27648 B
+    # (dk 128), 15360 B (dk 64); bf16 inputs: one per (b, h, pair of chunks):
+    # 29696 B (dk 128), 17408 B (dk 64)
+    assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == 32 * 2048 * 29696
+    assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == 64 * 128 * 29696
+    assert binding.kda_chunk_fwd_workspace_size(1, 33, 2, 64, 64, BF16) == 2 * 2 * 17408
     assert binding.kda_chunk_fwd_workspace_size(1, 256, 2, 64, 64, F32) == 2 * 16 * 15360
     assert binding.kda_chunk_fwd_workspace_size(1, 17, 1, 128, 128, F32) == 2 * 27648
     assert binding.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, F32) == 0
@@ -211,7 +213,8 @@ def test_chunk_ex_check_gate_and_snapshots(lib):
     assert check_ex(lib, p, sz, gate=1) == OK
     assert check_ex(lib, p, sz, gate=2) == UNSUP
     assert check_ex(lib, p, sz, snaps=snaps, every=512) == OK
-    assert check_ex(lib, p, sz, snaps=snaps, every=16) == OK
+    assert check_ex(lib, p, sz, snaps=snaps, every=32) == OK
+    assert check_ex(lib, p, sz, snaps=snaps, every=16) == UNSUP   # whole 32-token steps
     assert check_ex(lib, p, sz, snaps=None, every=512) == NULL
     assert check_ex(lib, p, sz, snaps=None, every=2048) == OK      # none falls inside T
     assert check_ex(lib, p, sz, snaps=snaps, every=-16) == SHAPE

@@ -47,7 +47,8 @@ def _oracle(ins, gate=0):
 
 # ---------------------------------------------------------------- snapshots
 
-@pytest.mark.parametrize("dt,T,every", [("bf16", 1100, 512), ("f32", 200, 16), ("bf16", 1024, 256)])
+@pytest.mark.parametrize("dt,T,every", [("bf16", 1100, 512), ("f32", 200, 32), ("bf16", 1024, 256),
+                                        ("bf16", 200, 32)])
 def test_snapshots_match_oracle_prefix_states(dt, T, every):
     announce("snapshots", dt, "T", T, "every", every)
     ins = inputs.make_forward(2, T, 3, 128, 64, dt, s0="normal", seed=T + every, device=DEV)

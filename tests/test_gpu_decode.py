@@ -84,3 +84,17 @@ def test_decode_equals_prefill():
     o_pf, S_pf = gpu_forward(ins)
     assert rel_err(o_pf.transpose(0, 1).cpu().numpy(), o_dec.cpu().numpy()) <= TOL["bf16"]
     assert rel_err(S_pf.cpu().numpy(), S_dec.cpu().numpy()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_decode_more_units_than_workgroups(dk, dv):
+    # 40 x 27 = 1080 (request, head) units against a grid of at most 1024
+    # persistent workgroups: some take two units, which exercises the
+    # prefetch of the next state and the last unit of each workgroup.
+    N, H = 40, 27
+    announce("decode ragged persistent", N, H, dk, dv)
+    d = inputs.make_decode(N, 2, H, dk, dv, "bf16", seed=41 + dk, device=DEV)
+    o, S = run_steps(d)
+    o_ref, S_ref = oracle_steps(d)
+    assert rel_err(o.cpu().numpy(), o_ref) <= 1e-4
+    assert rel_err(S.cpu().numpy(), S_ref) <= 1e-4

@@ -173,6 +173,28 @@ def test_spec_commit_replays_the_accepted_prefix(dt):
         assert e <= 1e-4, (n, a, e)
 
 
+def test_spec_commit_more_units_than_workgroups():
+    # 41 x 26 = 1066 units against at most 1024 persistent workgroups, with
+    # a different accepted count per request (zero included): the prefetch
+    # chain must skip nothing when a unit replays no token.
+    N, T, H, dk, dv = 41, 3, 26, 64, 64
+    announce("spec commit ragged persistent")
+    ins = _spec_inputs(N, T, H, dk, dv, "bf16", seed=43)
+    acc_list = [(7 * n) % (T + 1) for n in range(N)]
+    accepted = torch.tensor(acc_list, dtype=torch.int32, device=DEV)
+    S = ins["S0"].clone()
+    binding.kda_spec_commit(ins["k"], ins["v"], ins["g"], ins["beta"], S, accepted)
+    torch.cuda.synchronize()
+    for n, a in enumerate(acc_list):
+        if a == 0:
+            assert torch.equal(S[n], ins["S0"][n])
+            continue
+        one = {m: ins[m][n:n + 1, :a].contiguous() for m in ("q", "k", "v", "g", "beta")}
+        one["S0"] = ins["S0"][n:n + 1]
+        _, S_ref = _oracle(one)
+        assert rel_err(S[n].cpu().numpy(), S_ref[0]) <= 1e-4, (n, a)
+
+
 def test_spec_round_trip_equals_plain_decoding():
     # verify 6 drafts, accept a per-request prefix, commit; then decode the
     # next token: same outputs and state as decoding the accepted tokens and

@@ -724,6 +724,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // LDS-only release/acquire around a workgroup barrier: orders this wave's LDS
 // accesses against the other wave's, without waiting for global loads. The
@@ -742,7 +743,11 @@ template <int DK>
 struct Ring32Geom {
   static constexpr int kRec = DK == 128 ? 29696 : 17408;  // pair record bytes (pair_layout)
   static constexpr int kUnits = kRec / 1024;              // 16-byte record loads per lane
-  static constexpr int kSlot = kRec + 1024;               // + two V^T tiles, 16x16 fp16
+  // + two V^T tiles (16 columns x 16 tokens fp16), rows padded to 10 dwords
+  // so that the loader's transposing writes hit 64 different LDS banks
+  static constexpr int kVPitch = 40;                      // bytes per column row
+  static constexpr int kVTile = 16 * kVPitch;             // bytes per chunk
+  static constexpr int kSlot = kRec + 2 * kVTile;
   // Four slots let the loaders run up to three pairs ahead of the compute
   // wave, which absorbs the jitter of either side (measured on the 64K-token
   // workload: 3 slots 1.48-1.51 ms, 4 slots 1.46-1.48, 5 slots 1.50).
@@ -754,16 +759,16 @@ struct Ring32Geom {
   // 1.51 ms, two 1.48, three 1.52).
   static constexpr int kLoaders = 2;
   static constexpr int kUnitsPer = (kUnits + kLoaders - 1) / kLoaders;
-  static constexpr int kStagesRaw = 1 + 63 / (kUnitsPer + 1);
+  static constexpr int kStagesRaw = 1 + 63 / (kUnitsPer + 2);  // + two V loads
   static constexpr int kStages = kStagesRaw > 5 ? 5 : kStagesRaw;
-  static_assert((kStages - 1) * (kUnitsPer + 1) <= 63, "loads in flight exceed the wait counter");
+  static_assert((kStages - 1) * (kUnitsPer + 2) <= 63, "loads in flight exceed the wait counter");
 };
 
 template <int DK>
 struct Loader32Stage {
   u32x4 r[Ring32Geom<DK>::kUnitsPer];
-  u32x4 v;
-  bool v_ok;
+  u32x2 v0, v1;  // tokens 2a and 2a + 1, four columns each (bf16)
+  bool ok0, ok1;
 };
 
 template <int DK>
@@ -796,9 +801,9 @@ struct PairFrags {
     tc2 = ld_at<f16x8>(slot + L.tc2, lo);
     tb1 = ld_at<f16x4>(slot + L.tb1, static_cast<uint32_t>(l) * 8);
     const uint8_t* vt = slot + Ring32Geom<DK>::kRec;
-    const uint32_t vo = static_cast<uint32_t>(c16 * 16 + 4 * gq) * 2;
+    const uint32_t vo = static_cast<uint32_t>(c16 * Ring32Geom<DK>::kVPitch + 8 * gq);
     v1 = ld_at<f16x4>(vt, vo);
-    v2 = ld_at<f16x4>(vt + 512, vo);
+    v2 = ld_at<f16x4>(vt + Ring32Geom<DK>::kVTile, vo);
   }
 };
 
@@ -834,9 +839,10 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
   if (wave < kLd) {
     // ---------------- loaders ----------------
     const bool has_v = wave == kLd - 1;
-    // V: lane -> token tv of the pair (0..31), columns cv .. cv+7 of the slice
-    const int tv = l >> 1, cv = 8 * (l & 1);
-    const uint32_t vcol = static_cast<uint32_t>(slice * 16 + cv);
+    // V: lane -> tokens 2a, 2a + 1 of the pair (a = 0..15), columns 4cq ..
+    // 4cq + 3 of the slice
+    const int va = l & 15, cq = l >> 4;
+    const uint32_t vcol = static_cast<uint32_t>(slice * 16 + 4 * cq);
     const uint32_t vrow = static_cast<uint32_t>(H * DV);  // elements per token
     const uint16_t* vb = v + hb;
     // Loads are unconditional (pairs past the end re-read the last one; V
@@ -852,9 +858,13 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
       }
       if (has_v) {
         const int64_t tmax = T - 1 - cc * 32;
-        const uint32_t tt = static_cast<uint32_t>(tv < tmax ? tv : tmax);
-        st.v = ld_at<u32x4>(vb + static_cast<size_t>(cc) * pair_elems, (tt * vrow + vcol) * 2u);
-        st.v_ok = c * 32 + tv < T;
+        const uint32_t t0 = static_cast<uint32_t>(2 * va < tmax ? 2 * va : tmax);
+        const uint32_t t1 = static_cast<uint32_t>(2 * va + 1 < tmax ? 2 * va + 1 : tmax);
+        const uint16_t* vp = vb + static_cast<size_t>(cc) * pair_elems;
+        st.v0 = ld_at<u32x2>(vp, (t0 * vrow + vcol) * 2u);
+        st.v1 = ld_at<u32x2>(vp, (t1 * vrow + vcol) * 2u);
+        st.ok0 = c * 32 + 2 * va < T;
+        st.ok1 = c * 32 + 2 * va + 1 < T;
       }
     };
     // Commits are unconditional too: a pair past the end lands in a slot the
@@ -867,14 +877,21 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
         if (j < G::kUnits) st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[u]);
       }
       if (has_v) {
-        // V^T[col][token] in fp16, one 16x16 tile per chunk of the pair: the
-        // compute lane (c16, gq) reads tokens 4gq .. 4gq+3 of column c16.
-        _Float16* vt = reinterpret_cast<_Float16*>(dst + G::kRec) + (tv >> 4) * 256 + (tv & 15);
+        // V^T[col][token] in fp16, one tile per chunk of the pair (rows of
+        // G::kVPitch bytes): the compute lane (c16, gq) reads tokens 4gq ..
+        // 4gq+3 of column c16. This lane writes tokens 2a, 2a + 1 of its four
+        // columns, one dword each.
+        uint8_t* vt = dst + G::kRec + (va >> 3) * G::kVTile + (va & 7) * 4;
+        const uint32_t r0[2] = {st.ok0 ? st.v0[0] : 0u, st.ok0 ? st.v0[1] : 0u};
+        const uint32_t r1[2] = {st.ok1 ? st.v1[0] : 0u, st.ok1 ? st.v1[1] : 0u};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t x = st.v_ok ? st.v[i] : 0u;
-          vt[(cv + 2 * i) * 16] = static_cast<_Float16>(__uint_as_float(x << 16));
-          vt[(cv + 2 * i + 1) * 16] = static_cast<_Float16>(__uint_as_float(x & 0xffff0000u));
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t b0 = (c & 1) ? (r0[c >> 1] & 0xffff0000u) : (r0[c >> 1] << 16);
+          const uint32_t b1 = (c & 1) ? (r1[c >> 1] & 0xffff0000u) : (r1[c >> 1] << 16);
+          f16x2 h;
+          h[0] = static_cast<_Float16>(__uint_as_float(b0));
+          h[1] = static_cast<_Float16>(__uint_as_float(b1));
+          *reinterpret_cast<f16x2*>(vt + (4 * cq + c) * G::kVPitch) = h;
         }
       }
     };

@@ -32,10 +32,13 @@ def ring_constants(dk):
     k_slots = int(re.search(r"kSlots = (\d+);", geom).group(1))
     k_loaders = int(re.search(r"kLoaders = (\d+);", geom).group(1))
     max_stages = int(re.search(r"kStagesRaw > (\d+) \? \d+ : kStagesRaw", geom).group(1))
+    v_loads = int(re.search(r"kStagesRaw = 1 \+ 63 / \(kUnitsPer \+ (\d+)\)", geom).group(1))
+    v_pitch = int(re.search(r"kVPitch = (\d+);", geom).group(1))
     units = k_rec // 1024
     per = (units + k_loaders - 1) // k_loaders
-    stages = min(max_stages, 1 + 63 // (per + 1))
-    return dict(slots=k_slots, loaders=k_loaders, units=units, per=per, stages=stages)
+    stages = min(max_stages, 1 + 63 // (per + v_loads))
+    return dict(slots=k_slots, loaders=k_loaders, units=units, per=per, stages=stages,
+                v_loads=v_loads, slot_bytes=k_rec + 2 * 16 * v_pitch)
 
 
 def simulate(T, slots, stages):
@@ -85,11 +88,10 @@ def simulate(T, slots, stages):
 @pytest.mark.parametrize("dk", [128, 64])
 def test_constants_fit_the_wait_counter_and_lds(dk):
     c = ring_constants(dk)
-    # the loader that also loads V keeps per + 1 loads per pair in flight
-    assert (c["stages"] - 1) * (c["per"] + 1) <= 63
+    # the loader that also loads V keeps per + v_loads loads per pair in flight
+    assert (c["stages"] - 1) * (c["per"] + c["v_loads"]) <= 63
     assert c["per"] * c["loaders"] >= c["units"]
-    slot = (c["units"] * 1024) + 1024
-    assert c["slots"] * slot <= 160 * 1024
+    assert c["slots"] * c["slot_bytes"] <= 160 * 1024
     assert c["slots"] >= 2 and c["stages"] >= 1
 
 

@@ -60,7 +60,7 @@ def load_traffic(kernel):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
@@ -195,6 +195,7 @@ def main():
         "roofline": roofs[dominant],
         "prefill": {
             "tokens_per_s": round(value, 1), "ms": round(prefill_ms.mean(), 4),
+            "median_ms": round(float(np.median(prefill_ms)), 4),
             "prep_ms": round(prep_ms.mean(), 4), "state_pass_ms": round(pass_ms.mean(), 4),
             "algorithmic_GBps": round(prefill_gbps, 1),
             "frac_of_hbm_roof": round(prefill_gbps / HBM_PEAK_GBPS, 4),
@@ -206,7 +207,8 @@ def main():
             "state_GBps": round(dec_state_bytes / (dec_ms.mean() * 1e-3) / 1e9, 1),
             "all_GBps": round(dec_bytes / (dec_ms.mean() * 1e-3) / 1e9, 1),
             "frac_of_hbm_roof": round(dec_bytes / (dec_ms.mean() * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "us_per_step": round(dec_ms.mean() * 1e3, 2), "steps_per_launch_set": steps,
+            "us_per_step": round(dec_ms.mean() * 1e3, 2), "median_us_per_step": round(float(np.median(dec_ms)) * 1e3, 2),
+            "steps_per_launch_set": steps,
         },
         "kernels": roofs,
         "next": nxt,

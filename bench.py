@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KDA prefill tokens/s (H=32,d=128,T=64K) + decode state GB/s, % of roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -66,7 +67,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens (all 32 heads) of the prefill workload the oracle runs")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the snapshot / speculative-decoding measurements (profiling runs)")
+                    help="skip the snapshot / speculative-decoding measurements and the other "
+                         "forward workloads (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -213,6 +215,11 @@ def main():
         "kernels": roofs,
         "next": nxt,
     }
+    if not args.no_next:
+        # the other forward workloads, one after another, after the 64K inputs are released
+        del ws
+        torch.cuda.empty_cache()
+        rec["other_workloads"] = measure_workloads(binding, configs, inputs, stream, dev, np, torch)
 
     # practical HBM ceiling for context: a plain device-to-device copy
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -293,6 +300,54 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
                  "decode_step_us": round(dec_ms * 1e3, 2),
                  "verify_plus_commit_vs_decode_steps": round((ver_ms + com_ms) / (draft * dec_ms), 4)},
     }
+
+
+def measure_workloads(binding, configs, inputs, stream, dev, np, torch):
+    """kda_chunk_fwd (prep + state pass) on the forward workloads other than
+    the 64K prefill, each timed with HIP events around its two launches."""
+    out = []
+    for w in (configs.SMALL_FWD, configs.MID_FWD, configs.PREFILL_1M):
+        print("[bench] workload %s" % w.name, file=sys.stderr, flush=True)
+        ins = inputs.make_workload(w, device=dev)
+        code = 0 if w.in_dtype == "f32" else 1
+        ws = torch.empty(binding.kda_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, code),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device=dev)
+        ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+        reps = 3 if w.T > 65536 else 10
+        prep, pas = [], []
+        for r in range(reps + 2):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            binding.kda_chunk_prep(ins["q"], ins["k"], ins["g"], ins["beta"], w.dv, workspace=ws)
+            e[1].record(stream)
+            binding.kda_chunk_state_pass(ins["v"], ws, w.dk, ins["S0"], o=o, S_T=ST)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            if r >= 2:  # two warm-up runs
+                prep.append(e[0].elapsed_time(e[1]))
+                pas.append(e[1].elapsed_time(e[2]))
+        ms = float(np.mean(np.add(prep, pas)))
+        th = w.B * w.T * w.H
+        es = 4 if code == 0 else 2
+        flops = 6 * w.dk * w.dv + 4 * 16 * w.dk + 2 * 16 * w.dv + 16 * (w.dk + w.dv)
+        nbytes = th * (es * (3 * w.dk + w.dv + 1) + 4 * w.dv) + w.B * w.H * w.dk * w.dv * 4 * \
+            (2 if ins["S0"] is not None else 1)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        tflops = th * flops / (ms * 1e-3) / 1e12
+        # matrix-core peak of the path's own operand type: fp32 products for
+        # fp32 inputs, fp16/bf16 products for bf16 inputs
+        peak = FP32_MFMA_PEAK_TFLOPS if code == 0 else BF16_MFMA_PEAK_TFLOPS
+        out.append({"workload": w.name, "in_dtype": w.in_dtype, "B": w.B, "T": w.T, "H": w.H,
+                    "dk": w.dk, "dv": w.dv, "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+                    "ms": round(ms, 4), "prep_ms": round(float(np.mean(prep)), 4),
+                    "state_pass_ms": round(float(np.mean(pas)), 4), "timed_runs": reps,
+                    "algorithmic_GBps": round(gbps, 1), "frac_of_hbm_roof": round(gbps / HBM_PEAK_GBPS, 4),
+                    "algorithmic_TFLOPs": round(tflops, 3),
+                    "frac_of_matrix_peak": round(tflops / peak, 5), "matrix_peak_TFLOPs": peak})
+        del ins, ws, o, ST
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_leg(ins, o, ntok, pf):

@@ -739,35 +739,42 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int DK>
+template <int DK, int SPW>
 struct Ring32Geom {
   static constexpr int kRec = DK == 128 ? 29696 : 17408;  // pair record bytes (pair_layout)
   static constexpr int kUnits = kRec / 1024;              // 16-byte record loads per lane
-  // + two V^T tiles (16 columns x 16 tokens fp16), rows padded to 10 dwords
-  // so that the loader's transposing writes hit 64 different LDS banks
+  // + two V^T tiles (16 columns x 16 tokens fp16) per slice of the workgroup,
+  // rows padded to 10 dwords so that the loader's transposing writes hit 64
+  // different LDS banks
   static constexpr int kVPitch = 40;                      // bytes per column row
   static constexpr int kVTile = 16 * kVPitch;             // bytes per chunk
-  static constexpr int kSlot = kRec + 2 * kVTile;
+  static constexpr int kSlot = kRec + SPW * 2 * kVTile;
   // Four slots let the loaders run up to three pairs ahead of the compute
   // wave, which absorbs the jitter of either side (measured on the 64K-token
   // workload: 3 slots 1.48-1.51 ms, 4 slots 1.46-1.48, 5 slots 1.50).
   static constexpr int kSlots = 4;
   // loader wavefronts: loader w loads record units j = w, w + kLoaders, ...;
-  // the last one also loads V. Each has its own load counter, so each can
-  // keep more pairs in flight: kStages - 1 pairs of its loads stay
-  // outstanding at each commit, within the 6-bit wait counter (one loader
-  // 1.51 ms, two 1.48, three 1.52).
+  // the last one also loads V (two loads per slice). Each has its own load
+  // counter, so each can keep more pairs in flight: kStages - 1 pairs of its
+  // loads stay outstanding at each commit, within the 6-bit wait counter (one
+  // loader 1.51 ms, two 1.48, three 1.52).
   static constexpr int kLoaders = 2;
   static constexpr int kUnitsPer = (kUnits + kLoaders - 1) / kLoaders;
-  static constexpr int kStagesRaw = 1 + 63 / (kUnitsPer + 2);  // + two V loads
+  static constexpr int kStagesRaw = 1 + 63 / (kUnitsPer + 2 * SPW);  // + the V loads
   static constexpr int kStages = kStagesRaw > 5 ? 5 : kStagesRaw;
-  static_assert((kStages - 1) * (kUnitsPer + 2) <= 63, "loads in flight exceed the wait counter");
+  static_assert((kStages - 1) * (kUnitsPer + 2 * SPW) <= 63, "loads in flight exceed the wait counter");
 };
 
-template <int DK>
+// Time per 32-token step of a workgroup serving 2 or 4 slices, relative to one
+// slice per workgroup (measured with 32 heads of 128 x 128 over 64K tokens,
+// one workgroup per compute unit: 1.47, 1.65 and 2.04 ms).
+constexpr double kSpw2StepCost = 1.12;
+constexpr double kSpw4StepCost = 1.38;
+
+template <int DK, int SPW>
 struct Loader32Stage {
-  u32x4 r[Ring32Geom<DK>::kUnitsPer];
-  u32x2 v0, v1;  // tokens 2a and 2a + 1, four columns each (bf16)
+  u32x4 r[Ring32Geom<DK, SPW>::kUnitsPer];
+  u32x2 v0[SPW], v1[SPW];  // tokens 2a and 2a + 1, four columns of each slice (bf16)
   bool ok0, ok1;
 };
 
@@ -780,7 +787,10 @@ struct PairFrags {
   f16x4 tb1, v1, v2;
   f32x4 eg[NM];
 
-  __device__ __forceinline__ void load(const uint8_t* slot, const PairLayout& L, int l, int gq, int c16) {
+  // vt: this slice's two V^T tiles (rows of kVPitch bytes, kVTile apart)
+  template <int kVPitch, int kVTile>
+  __device__ __forceinline__ void load(const uint8_t* slot, const uint8_t* vt, const PairLayout& L, int l,
+                                       int gq, int c16) {
 #pragma unroll
     for (int p = 0; p < NM / 2; ++p) {
       const uint32_t off = static_cast<uint32_t>(p * 64 + l) * 16;
@@ -800,33 +810,34 @@ struct PairFrags {
     m2l = ld_at<f16x8>(slot + L.m2l, lo);
     tc2 = ld_at<f16x8>(slot + L.tc2, lo);
     tb1 = ld_at<f16x4>(slot + L.tb1, static_cast<uint32_t>(l) * 8);
-    const uint8_t* vt = slot + Ring32Geom<DK>::kRec;
-    const uint32_t vo = static_cast<uint32_t>(c16 * Ring32Geom<DK>::kVPitch + 8 * gq);
+    const uint32_t vo = static_cast<uint32_t>(c16 * kVPitch + 8 * gq);
     v1 = ld_at<f16x4>(vt, vo);
-    v2 = ld_at<f16x4>(vt + Ring32Geom<DK>::kVTile, vo);
+    v2 = ld_at<f16x4>(vt + kVTile, vo);
   }
 };
 
-template <typename OutT, int DK>
-__global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state_pass_ring32(const uint16_t* __restrict__ v,
-                                                             const uint8_t* __restrict__ ws,
-                                                             const float* S0, OutT* __restrict__ o,
-                                                             float* ST, float* __restrict__ snap,
-                                                             int64_t snap_pairs, int64_t T,
-                                                             int64_t H, int64_t DV, int64_t NPR,
-                                                             int64_t nslices, int64_t nheads,
-                                                             PairLayout L) {
-  using G = Ring32Geom<DK>;
+// With SPW > 1, one workgroup serves SPW consecutive 16-column slices of a
+// head: one compute wavefront per slice, all reading the same record from the
+// shared ring, and the V loader loads every slice's V tiles. A compute unit
+// then advances SPW slices at once, for workloads with more slices than
+// compute units.
+template <typename OutT, int DK, int SPW>
+__global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kda_state_pass_ring32(
+    const uint16_t* __restrict__ v, const uint8_t* __restrict__ ws, const float* S0,
+    OutT* __restrict__ o, float* ST, float* __restrict__ snap, int64_t snap_pairs, int64_t T,
+    int64_t H, int64_t DV, int64_t NPR, int64_t ngroups, int64_t nheads, PairLayout L) {
+  using G = Ring32Geom<DK, SPW>;
   constexpr int NM = DK / 16;
   constexpr int kR = G::kSlots, kS = G::kStages;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kR * G::kSlot];
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, c16 = l & 15, gq = l >> 4;
-  // XCD-aware numbering, as in kda_state_pass.
+  // XCD-aware numbering, as in kda_state_pass: all slice groups of a head
+  // have ids congruent mod 8 and share one XCD's L2 for the head's records.
   const int64_t wgid = blockIdx.x;
   const int64_t xcd = wgid & 7, kk = wgid >> 3;
-  const int64_t head = xcd + 8 * (kk / nslices);
-  const int64_t slice = kk % nslices;
+  const int64_t head = xcd + 8 * (kk / ngroups);
+  const int64_t group = kk % ngroups;
   if (head >= nheads) return;  // whole workgroup
   const int64_t b = head / H, h = head % H;
   const uint8_t* rec0 = ws + static_cast<size_t>(head) * NPR * G::kRec;
@@ -840,15 +851,15 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
     // ---------------- loaders ----------------
     const bool has_v = wave == kLd - 1;
     // V: lane -> tokens 2a, 2a + 1 of the pair (a = 0..15), columns 4cq ..
-    // 4cq + 3 of the slice
+    // 4cq + 3 of each slice of the group
     const int va = l & 15, cq = l >> 4;
-    const uint32_t vcol = static_cast<uint32_t>(slice * 16 + 4 * cq);
+    const uint32_t vcol = static_cast<uint32_t>(group * SPW * 16 + 4 * cq);
     const uint32_t vrow = static_cast<uint32_t>(H * DV);  // elements per token
     const uint16_t* vb = v + hb;
     // Loads are unconditional (pairs past the end re-read the last one; V
     // tokens past T read the last token and are zeroed at commit): a branch
     // around them would make the compiler's wait counting conservative.
-    auto issue = [&](Loader32Stage<DK>& st, int64_t c) __attribute__((always_inline)) {
+    auto issue = [&](Loader32Stage<DK, SPW>& st, int64_t c) __attribute__((always_inline)) {
       const int64_t cc = c < NPR ? c : NPR - 1;
       const uint8_t* src = rec0 + static_cast<size_t>(cc) * G::kRec;
 #pragma unroll
@@ -861,15 +872,18 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
         const uint32_t t0 = static_cast<uint32_t>(2 * va < tmax ? 2 * va : tmax);
         const uint32_t t1 = static_cast<uint32_t>(2 * va + 1 < tmax ? 2 * va + 1 : tmax);
         const uint16_t* vp = vb + static_cast<size_t>(cc) * pair_elems;
-        st.v0 = ld_at<u32x2>(vp, (t0 * vrow + vcol) * 2u);
-        st.v1 = ld_at<u32x2>(vp, (t1 * vrow + vcol) * 2u);
+#pragma unroll
+        for (int z = 0; z < SPW; ++z) {
+          st.v0[z] = ld_at<u32x2>(vp, (t0 * vrow + vcol + 16 * z) * 2u);
+          st.v1[z] = ld_at<u32x2>(vp, (t1 * vrow + vcol + 16 * z) * 2u);
+        }
         st.ok0 = c * 32 + 2 * va < T;
         st.ok1 = c * 32 + 2 * va + 1 < T;
       }
     };
     // Commits are unconditional too: a pair past the end lands in a slot the
     // compute wave reads no more, and is never read.
-    auto commit = [&](const Loader32Stage<DK>& st, int64_t c) __attribute__((always_inline)) {
+    auto commit = [&](const Loader32Stage<DK, SPW>& st, int64_t c) __attribute__((always_inline)) {
       uint8_t* dst = ring + static_cast<int>(c % kR) * G::kSlot;
 #pragma unroll
       for (int u = 0; u < G::kUnitsPer; ++u) {
@@ -878,24 +892,27 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
       }
       if (has_v) {
         // V^T[col][token] in fp16, one tile per chunk of the pair (rows of
-        // G::kVPitch bytes): the compute lane (c16, gq) reads tokens 4gq ..
-        // 4gq+3 of column c16. This lane writes tokens 2a, 2a + 1 of its four
-        // columns, one dword each.
-        uint8_t* vt = dst + G::kRec + (va >> 3) * G::kVTile + (va & 7) * 4;
-        const uint32_t r0[2] = {st.ok0 ? st.v0[0] : 0u, st.ok0 ? st.v0[1] : 0u};
-        const uint32_t r1[2] = {st.ok1 ? st.v1[0] : 0u, st.ok1 ? st.v1[1] : 0u};
+        // G::kVPitch bytes), two tiles per slice: the compute lane (c16, gq)
+        // reads tokens 4gq .. 4gq+3 of column c16. This lane writes tokens
+        // 2a, 2a + 1 of its four columns of each slice, one dword each.
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t b0 = (c & 1) ? (r0[c >> 1] & 0xffff0000u) : (r0[c >> 1] << 16);
-          const uint32_t b1 = (c & 1) ? (r1[c >> 1] & 0xffff0000u) : (r1[c >> 1] << 16);
-          f16x2 h;
-          h[0] = static_cast<_Float16>(__uint_as_float(b0));
-          h[1] = static_cast<_Float16>(__uint_as_float(b1));
-          *reinterpret_cast<f16x2*>(vt + (4 * cq + c) * G::kVPitch) = h;
+        for (int z = 0; z < SPW; ++z) {
+          uint8_t* vt = dst + G::kRec + (2 * z + (va >> 3)) * G::kVTile + (va & 7) * 4;
+          const uint32_t r0[2] = {st.ok0 ? st.v0[z][0] : 0u, st.ok0 ? st.v0[z][1] : 0u};
+          const uint32_t r1[2] = {st.ok1 ? st.v1[z][0] : 0u, st.ok1 ? st.v1[z][1] : 0u};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t b0 = (c & 1) ? (r0[c >> 1] & 0xffff0000u) : (r0[c >> 1] << 16);
+            const uint32_t b1 = (c & 1) ? (r1[c >> 1] & 0xffff0000u) : (r1[c >> 1] << 16);
+            f16x2 hv;
+            hv[0] = static_cast<_Float16>(__uint_as_float(b0));
+            hv[1] = static_cast<_Float16>(__uint_as_float(b1));
+            *reinterpret_cast<f16x2*>(vt + (4 * cq + c) * G::kVPitch) = hv;
+          }
         }
       }
     };
-    Loader32Stage<DK> st[kS];
+    Loader32Stage<DK, SPW> st[kS];
 #pragma unroll
     for (int c = 0; c < kS; ++c) issue(st[c], c);
 #pragma unroll
@@ -919,6 +936,8 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
   }
 
   // ---------------- compute ----------------
+  const int z = wave - kLd;  // this wavefront's slice within the group
+  const int64_t slice = group * SPW + z;
   const int64_t col = slice * 16 + c16;
   f32x4 S[NM];
   const size_t sbase = static_cast<size_t>(head) * DK * DV + col;
@@ -942,7 +961,8 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK>::kLoaders + 1)) void kda_state
   ring_barrier();
   for (int64_t n = 0; n < NPR; ++n) {
     PairFrags<DK> f;
-    f.load(ring + static_cast<int>(n % kR) * G::kSlot, L, l, gq, c16);
+    const uint8_t* slot = ring + static_cast<int>(n % kR) * G::kSlot;
+    f.template load<G::kVPitch, G::kVTile>(slot, slot + G::kRec + 2 * z * G::kVTile, L, l, gq, c16);
     f16x8 sh[NM / 2];
 #pragma unroll
     for (int p = 0; p < NM / 2; ++p)
@@ -1022,7 +1042,7 @@ template <typename InT, int DK, int GATE>
 hipError_t launch_prep_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   if constexpr (!kIsF32<InT>) {  // bf16 inputs: one record per pair of chunks
     const PairLayout L = pair_layout(DK);
-    if (L.bytes != Ring32Geom<DK>::kRec) return hipErrorInvalidValue;
+    if (L.bytes != Ring32Geom<DK, 1>::kRec) return hipErrorInvalidValue;
     const int64_t NPR = (a.T + 31) / 32;
     const int64_t blocks = a.B * NPR * a.H;
     hipLaunchKernelGGL((kda_chunk_prep_pair<DK, GATE>), dim3(static_cast<uint32_t>(blocks)),
@@ -1049,6 +1069,48 @@ inline bool wants_snapshots(const ChunkFwdArgs& a) {
   return a.snapshots != nullptr && a.snapshot_every > 0 && a.T >= a.snapshot_every;
 }
 
+template <typename OutT, int DK, int SPW>
+hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t stream) {
+  using G = Ring32Geom<DK, SPW>;
+  const PairLayout P = pair_layout(DK);
+  if (P.bytes != G::kRec) return hipErrorInvalidValue;  // layout and ring disagree
+  const int64_t NPR = (a.T + 31) / 32;
+  const int64_t ngroups = a.dv / 16 / SPW;
+  const int64_t nheads = a.B * a.H;
+  const int64_t blocks = 8 * ngroups * ((nheads + 7) / 8);
+  hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK, SPW>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * (G::kLoaders + SPW)), 0, stream, static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o), a.S_T,
+                     snap_pairs > 0 ? a.snapshots : nullptr, snap_pairs, a.T, a.H, a.dv, NPR, ngroups,
+                     nheads, P);
+  return hipGetLastError();
+}
+
+// Slices per state-pass workgroup (1, 2 or 4, a divisor of the slice count).
+// Each workgroup runs the sequential chains of its slices. Estimated time:
+// (workgroups per compute unit, rounded up) x (relative time per step).
+// Workgroups that share a compute unit (dk = 64 rings leave room for two)
+// share its issue slots and LDS as well, so the estimate counts them as
+// taking turns. This picks the fastest variant in every case measured: 32 to
+// 256 heads, dk 64 and 128, dv 64 and 128 (e.g. 64 heads of 128 x 128: 0.205,
+// 0.136, 0.159 ms for 1, 2, 4 slices; 128 heads: 0.770, 0.482, 0.377 ms).
+inline int choose_slices_per_wg(int64_t nheads, int64_t nslices, int cus) {
+  const double step[3] = {1.0, kSpw2StepCost, kSpw4StepCost};
+  int best = 1;
+  double best_t = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int spw = 1 << i;
+    if (nslices % spw) continue;
+    const int64_t wgs = nheads * (nslices / spw);
+    const double t = static_cast<double>((wgs + cus - 1) / cus) * step[i];
+    if (i == 0 || t < best_t) {
+      best = spw;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 template <typename InT, typename OutT, int DK>
 hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   const int64_t nslices = a.dv / 16;
@@ -1056,16 +1118,16 @@ hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
   const int64_t snap_chunks = wants_snapshots(a) ? a.snapshot_every / 16 : 0;
   if constexpr (!kIsF32<InT>) {  // bf16 inputs: 32 tokens per step
-    const PairLayout P = pair_layout(DK);
-    if (P.bytes != Ring32Geom<DK>::kRec) return hipErrorInvalidValue;  // layout and ring disagree
-    const int64_t NPR = (a.T + 31) / 32;
     const int64_t snap_pairs = snap_chunks / 2;
-    hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64 * (Ring32Geom<DK>::kLoaders + 1)), 0, stream, static_cast<const uint16_t*>(a.v),
-                       static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
-                       a.S_T, snap_pairs > 0 ? a.snapshots : nullptr, snap_pairs, a.T, a.H, a.dv,
-                       NPR, nslices, nheads, P);
-    return hipGetLastError();
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidDevice;
+    switch (choose_slices_per_wg(nheads, nslices, cus > 0 ? cus : 1)) {
+      case 4: return launch_ring32<OutT, DK, 4>(a, snap_pairs, stream);
+      case 2: return launch_ring32<OutT, DK, 2>(a, snap_pairs, stream);
+      default: return launch_ring32<OutT, DK, 1>(a, snap_pairs, stream);
+    }
   } else {
     const RecordLayout L = record_layout(DK);
     const int64_t NC = (a.T + 15) / 16;

@@ -210,3 +210,58 @@ def test_stages_equal_forward_and_prep_is_reusable():
     ins2["S0"] = S0b
     o_ref2, S_ref2 = gpu_forward(ins2)
     assert torch.equal(o2, o_ref2) and torch.equal(S2, S_ref2)
+
+
+# Batched shapes with more 16-column head-slices than a 256-unit device has
+# compute units, so that the bf16 state pass serves 2 or 4 slices per
+# workgroup (compute wavefronts sharing one LDS ring). Each is checked against
+# the oracle and against the same sequences run one batch entry per call
+# (few slices: one per workgroup): the per-slice arithmetic is the same, so
+# the results must be bit-identical.
+MANY_HEADS = [
+    (4, 333, 16, 128, 128),   # 512 slices: 2 per workgroup
+    (8, 100, 16, 128, 128),   # 1024 slices: 4 per workgroup
+    (8, 77, 32, 64, 128),     # dk 64, 2048 slices: 4 per workgroup
+    (8, 50, 16, 64, 64),      # 512 slices of dv 64: 2 per workgroup
+    (16, 40, 16, 128, 48),    # 3 slices per head: one per workgroup
+]
+
+
+def _per_entry(ins, **kw):
+    B = ins["q"].shape[0]
+    outs = []
+    for b in range(B):
+        sub = {n: (x[b:b + 1].contiguous() if x is not None else None) for n, x in ins.items()}
+        outs.append(binding.kda_chunk_fwd_ex(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                                             sub["S0"], **kw))
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("shape", MANY_HEADS, ids=lambda s: "b%d_t%d_h%d_dk%d_dv%d" % s)
+def test_many_heads_share_workgroups(shape):
+    B, T, H, dk, dv = shape
+    seed = 500 + sum(shape)
+    announce("many heads", shape, "seed", seed)
+    ins = inputs.make_forward(B, T, H, dk, dv, "bf16", "normal", seed=seed, device=DEV)
+    o, ST = gpu_forward(ins)
+    for b, (ob, Sb, _) in enumerate(_per_entry(ins)):
+        assert torch.equal(ob, o[b:b + 1]) and torch.equal(Sb, ST[b:b + 1]), b
+    o_ref, S_ref = oracle_forward(ins)
+    eo, es = rel_err(o.cpu().numpy(), o_ref), rel_err(ST.cpu().numpy(), S_ref)
+    announce("  err_o=%.3g err_S=%.3g" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_many_heads_snapshots_and_bf16_output():
+    """Snapshots and bf16 output from workgroups of 4 slices, against per-entry calls."""
+    ins = inputs.make_forward(8, 200, 16, 128, 128, "bf16", "normal", seed=61, device=DEV)
+    announce("many heads: snapshots every 64, bf16 o")
+    kw = dict(snapshot_every=64, out_dtype=torch.bfloat16)
+    o, ST, sn = binding.kda_chunk_fwd_ex(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                         ins["S0"], **kw)
+    torch.cuda.synchronize()
+    assert sn.shape == (8, 3, 16, 128, 128)
+    for b, (ob, Sb, snb) in enumerate(_per_entry(ins, **kw)):
+        assert torch.equal(ob, o[b:b + 1]) and torch.equal(Sb, ST[b:b + 1])
+        assert torch.equal(snb, sn[b:b + 1])

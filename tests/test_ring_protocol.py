@@ -23,7 +23,7 @@ SRC = os.path.join(os.path.dirname(__file__), "..", "linear_attention_recurrence
                    "kda_chunk.hip")
 
 
-def ring_constants(dk):
+def ring_constants(dk, spw=1):
     text = open(SRC).read()
     geom = text[text.index("struct Ring32Geom"):]
     geom = geom[:geom.index("};")]
@@ -32,13 +32,15 @@ def ring_constants(dk):
     k_slots = int(re.search(r"kSlots = (\d+);", geom).group(1))
     k_loaders = int(re.search(r"kLoaders = (\d+);", geom).group(1))
     max_stages = int(re.search(r"kStagesRaw > (\d+) \? \d+ : kStagesRaw", geom).group(1))
-    v_loads = int(re.search(r"kStagesRaw = 1 \+ 63 / \(kUnitsPer \+ (\d+)\)", geom).group(1))
+    # the V loader adds two loads per slice of the workgroup (SPW slices)
+    per_slice = int(re.search(r"kStagesRaw = 1 \+ 63 / \(kUnitsPer \+ (\d+) \* SPW\)", geom).group(1))
+    v_loads = per_slice * spw
     v_pitch = int(re.search(r"kVPitch = (\d+);", geom).group(1))
     units = k_rec // 1024
     per = (units + k_loaders - 1) // k_loaders
     stages = min(max_stages, 1 + 63 // (per + v_loads))
     return dict(slots=k_slots, loaders=k_loaders, units=units, per=per, stages=stages,
-                v_loads=v_loads, slot_bytes=k_rec + 2 * 16 * v_pitch)
+                v_loads=v_loads, slot_bytes=k_rec + spw * 2 * 16 * v_pitch)
 
 
 def simulate(T, slots, stages):
@@ -85,9 +87,13 @@ def simulate(T, slots, stages):
     return loader_barriers, compute_barriers, writes, reads, slot_writes, NPR
 
 
+SPWS = [1, 2, 4]   # slices per workgroup the launcher instantiates
+
+
+@pytest.mark.parametrize("spw", SPWS)
 @pytest.mark.parametrize("dk", [128, 64])
-def test_constants_fit_the_wait_counter_and_lds(dk):
-    c = ring_constants(dk)
+def test_constants_fit_the_wait_counter_and_lds(dk, spw):
+    c = ring_constants(dk, spw)
     # the loader that also loads V keeps per + v_loads loads per pair in flight
     assert (c["stages"] - 1) * (c["per"] + c["v_loads"]) <= 63
     assert c["per"] * c["loaders"] >= c["units"]
@@ -95,9 +101,12 @@ def test_constants_fit_the_wait_counter_and_lds(dk):
     assert c["slots"] >= 2 and c["stages"] >= 1
 
 
+@pytest.mark.parametrize("spw", SPWS)
 @pytest.mark.parametrize("dk", [128, 64])
-def test_barriers_match_and_slots_never_race(dk):
-    c = ring_constants(dk)
+def test_barriers_match_and_slots_never_race(dk, spw):
+    # every compute wavefront of the workgroup runs the compute loop, so the
+    # counts below hold for each of them
+    c = ring_constants(dk, spw)
     for T in list(range(1, 700)) + [1023, 1024, 1025, 4095, 4096, 4097, 65536, 65537]:
         lb, cb, writes, reads, slot_writes, NPR = simulate(T, c["slots"], c["stages"])
         assert lb == cb, "barrier counts differ at T=%d" % T
@@ -137,3 +146,11 @@ def test_a_one_slot_ring_would_race():
                 later = [e for e, p in slot_writes[n % 1] if p > n]
                 if later:
                     assert min(later) >= reads[n] + 1
+
+
+def test_launcher_instantiates_the_modelled_slice_counts():
+    text = open(SRC).read()
+    launch = text[text.index("switch (choose_slices_per_wg("):]
+    launch = launch[:launch.index("}")]
+    found = sorted(int(x) for x in re.findall(r"launch_ring32<OutT, DK, (\d+)>", launch))
+    assert found == SPWS

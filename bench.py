@@ -371,9 +371,17 @@ def cpu_leg(ins, o, ntok, pf):
     wall = time.perf_counter() - t0
     og = o[:, :ntok].float().cpu().numpy()
     err = float(np.abs(og - o_ref).max() / np.sqrt(np.mean(o_ref ** 2)))
+    # per-core rate: the same tokens of one head on one thread
+    one = {n: np.ascontiguousarray(x[:, :, :1]) for n, x in host.items()}
+    t0 = time.perf_counter()
+    c_oracle.fwd(one["q"], one["k"], one["v"], one["g"], one["beta"], None, nthreads=1,
+                 want_state=False)
+    wall1 = time.perf_counter() - t0
     base = {"value": round(pf.B * ntok / wall, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "wall_s": round(wall, 2),
-            "sample": "fp64 C oracle, first %d of %d tokens, all %d heads of %s" % (ntok, pf.T, pf.H, pf.name)}
+            "sample": "fp64 C oracle, first %d of %d tokens, all %d heads of %s" % (ntok, pf.T, pf.H, pf.name),
+            "one_core": {"token_heads_per_s": round(pf.B * ntok / wall1, 1), "wall_s": round(wall1, 2),
+                         "sample": "the same tokens of head 0, one thread"}}
     parity = {"err_o_max_over_rms": err, "tokens": ntok, "heads": pf.H, "tolerance": 2e-2}
     return base, parity
 

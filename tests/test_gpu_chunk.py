@@ -265,3 +265,15 @@ def test_many_heads_snapshots_and_bf16_output():
     for b, (ob, Sb, snb) in enumerate(_per_entry(ins, **kw)):
         assert torch.equal(ob, o[b:b + 1]) and torch.equal(Sb, ST[b:b + 1])
         assert torch.equal(snb, sn[b:b + 1])
+
+
+@pytest.mark.parametrize("B", [4, 8], ids=["2_slices", "4_slices"])
+def test_many_heads_in_place_state(B):
+    """S_T = S0 (update in place) from workgroups of 2 and 4 slices."""
+    ins = inputs.make_forward(B, 150, 16, 128, 128, "bf16", "normal", seed=62 + B, device=DEV)
+    announce("many heads: in-place state, B", B)
+    o_ref, S_ref = gpu_forward(ins)
+    S = ins["S0"].clone()
+    o, _ = binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], S, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref) and torch.equal(o, o_ref)

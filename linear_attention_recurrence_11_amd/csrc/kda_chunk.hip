@@ -691,7 +691,9 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
 
 // ---------------------------------------------------------------------------
 // Sequential state pass, bf16 inputs: two loader wavefronts and a compute
-// wavefront per (b, h, 16-column slice), advancing 32 tokens per step.
+// wavefront per (b, h, 16-column slice), advancing 32 tokens per step (or one
+// compute wavefront for each of 2 or 4 slices of a head sharing the loaders,
+// when the slices outnumber the compute units).
 //
 // The compute wavefront keeps its dk x 16 slice of S in registers and runs
 // the sequential chain. Fed from global memory directly, a wavefront waits on
@@ -701,7 +703,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
 // its V tiles from HBM into a ring of LDS slots, several steps ahead, with
 // coalesced 16-byte loads (converting V to fp16, transposed for the MFMA
 // operand); the compute wavefront only reads LDS. One LDS-only barrier per
-// step keeps the three in step. Barrier 0 follows the loader's prologue,
+// step keeps them in step. Barrier 0 follows the loader's prologue,
 // barrier n + 1 ends step n:
 //   prologue         the loader fills slots 0 .. kSlots-2 with pairs
 //                    0 .. kSlots-2;

@@ -245,7 +245,8 @@ def main():
 def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, dev, np, torch,
                  reps=5, every=512, draft=4, accept=2):
     """The options built on the path, timed after the steps with HIP events:
-    the prefill with a state snapshot every `every` tokens (prefix reuse), and
+    the prefill with bf16 output, the prefill with a state snapshot every
+    `every` tokens (prefix reuse), and
     speculative verify of `draft` tokens + commit of `accept` of them for the
     decode batch, against the decode steps they replace."""
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -269,6 +270,10 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     plain_ms = timed(lambda: binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"],
                                                    ins["beta"], ins["S0"], o=o, S_T=ST, workspace=ws))
     del snaps
+    o16 = torch.empty(o.shape, dtype=torch.bfloat16, device=dev)
+    bf16_ms = timed(lambda: binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                                  ins["S0"], o=o16, S_T=ST, workspace=ws))
+    del o16
     N, Hd, dkd, dvd = d["S"].shape
     sp = inputs.make_forward(N, draft, Hd, dkd, dvd, "bf16", s0="zero", seed=4321, device=dev)
     Sck = d["S"].clone()
@@ -288,6 +293,8 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     com_bytes = 2 * state + draft * (tok_in - N * Hd * dkd * 2)
     del sp, Sck, Sw, o_sp
     return {
+        "bf16_output": {"prefill_ms": round(bf16_ms, 4), "plain_prefill_ms": round(plain_ms, 4),
+                        "tokens_per_s": round(B * T / (bf16_ms * 1e-3), 1)},
         "snapshots": {"every_tokens": every, "count": T // every,
                       "bytes": B * (T // every) * H * dk * dv * 4,
                       "prefill_ms": round(snap_ms, 4), "plain_prefill_ms": round(plain_ms, 4),

@@ -64,7 +64,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--cpu-tokens", type=int, default=65536,
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens (all 32 heads) of the prefill workload the oracle runs")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the snapshot / speculative-decoding measurements and the other "

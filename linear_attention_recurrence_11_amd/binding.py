@@ -103,6 +103,67 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else ctypes.c_void_p(0)
 
 
+def _check(what, specs):
+    """Validate every tensor handed to a C call before any pointer is taken.
+
+    specs: (name, tensor or None, shape tuple or None, allowed dtypes or None,
+    required). Checks, in this order: the argument is a torch.Tensor, its
+    dtype, its shape, contiguity, then that every tensor is a GPU tensor on
+    one device. Raises ValueError (TypeError for a non-tensor) naming the
+    argument; returns the common device. The library reads and writes exactly
+    the extents these shapes imply, so a mismatch here would otherwise be an
+    out-of-bounds access on the device."""
+    present = []
+    for name, t, shape, dtypes, required in specs:
+        if t is None:
+            if required:
+                raise ValueError("%s: %s is required" % (what, name))
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: %s must be a torch.Tensor, got %s" % (what, name, type(t).__name__))
+        if dtypes is not None and t.dtype not in dtypes:
+            raise ValueError("%s: %s has dtype %s, expected %s"
+                             % (what, name, t.dtype, " or ".join(str(d) for d in dtypes)))
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s: %s has shape %s, expected %s"
+                             % (what, name, tuple(t.shape), tuple(shape)))
+        if not t.is_contiguous():
+            raise ValueError("%s: %s must be contiguous" % (what, name))
+        present.append((name, t))
+    dev = None
+    for name, t in present:
+        if not t.is_cuda:
+            raise ValueError("%s: %s is on %s; every KDA tensor must be on the GPU"
+                             % (what, name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s: %s is on %s, other tensors on %s" % (what, name, t.device, dev))
+    return dev
+
+
+def _in_dtypes(x):
+    """The input dtype of a call, fixed by its first input tensor."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("KDA inputs must be torch tensors, got %s" % type(x).__name__)
+    _dcode(x.dtype)
+    return (x.dtype,)
+
+
+def _dims(x, n, what, name):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s: %s must be a torch.Tensor" % (what, name))
+    if x.dim() != n:
+        raise ValueError("%s: %s must have %d dimensions, got shape %s"
+                         % (what, name, n, tuple(x.shape)))
+    return tuple(x.shape)
+
+
+_F32 = (torch.float32,)
+_OUT = (torch.float32, torch.bfloat16)
+_U8 = None  # the workspace may be any dtype; its byte size is what counts
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -122,47 +183,74 @@ def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype):
     return int(_load().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
 
 
+def _fwd_specs(what, q, k, v, g, beta, S0, o, S_T, out_dtype):
+    B, T, H, dk = _dims(q, 4, what, "q")
+    dv = _dims(v, 4, what, "v")[-1]
+    dt = _in_dtypes(q)
+    specs = [("q", q, (B, T, H, dk), dt, True), ("k", k, (B, T, H, dk), dt, True),
+             ("v", v, (B, T, H, dv), dt, True), ("g", g, (B, T, H, dk), dt, True),
+             ("beta", beta, (B, T, H), dt, True), ("S0", S0, (B, H, dk, dv), _F32, False),
+             ("o", o, (B, T, H, dv), (out_dtype,) if o is None else _OUT, False),
+             ("S_T", S_T, (B, H, dk, dv), _F32, False)]
+    return (B, T, H, dk, dv), specs
+
+
+def _workspace(lib, what, workspace, need, dev):
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need > 0 else None
+    _check(what, [("workspace", workspace, None, _U8, True)])
+    if workspace.device != dev:
+        raise ValueError("%s: workspace is on %s, the inputs on %s" % (what, workspace.device, dev))
+    return workspace
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
 def kda_chunk_fwd(q, k, v, g, beta, S0=None, *, o=None, S_T=None, out_dtype=torch.float32,
                   want_state=True, workspace=None, stream=None):
     """Chunkwise KDA forward. q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]
     (all float32 or all bfloat16, on one GPU); S0 [B,H,dk,dv] float32 or None.
     Returns (o [B,T,H,dv] out_dtype, S_T [B,H,dk,dv] float32 or None).
     Pass S_T=S0 to update the state in place."""
+    what = "kda_chunk_fwd"
     lib = _load()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    (B, T, H, dk, dv), specs = _fwd_specs(what, q, k, v, g, beta, S0, o, S_T, out_dtype)
+    dev = _check(what, specs)
     code = _dcode(q.dtype)
-    dev = q.device
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     need = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    workspace = _workspace(lib, what, workspace, need, dev)
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
                            _ptr(S_T), B, T, H, dk, dv, code, _dcode(o.dtype), _ptr(workspace),
-                           wbytes, _stream(stream, dev))
+                           _nbytes(workspace), _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_chunk_fwd")
+        raise KDAError(st, what)
     return o, S_T
 
 
 def kda_chunk_prep(q, k, g, beta, dv, *, workspace=None, stream=None):
     """First stage of kda_chunk_fwd: per-chunk operands into a workspace
     (allocated here when not given). Returns the workspace tensor."""
+    what = "kda_chunk_prep"
     lib = _load()
-    B, T, H, dk = q.shape
+    B, T, H, dk = _dims(q, 4, what, "q")
+    dt = _in_dtypes(q)
+    dev = _check(what, [("q", q, (B, T, H, dk), dt, True), ("k", k, (B, T, H, dk), dt, True),
+                        ("g", g, (B, T, H, dk), dt, True), ("beta", beta, (B, T, H), dt, True)])
     code = _dcode(q.dtype)
     need = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    wbytes = workspace.numel() * workspace.element_size()
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace = _workspace(lib, what, workspace, need, dev)
     st = lib.kda_chunk_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), B, T, H, dk, dv, code,
-                            _ptr(workspace), wbytes, _stream(stream, q.device))
+                            _ptr(workspace), _nbytes(workspace), _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_chunk_prep")
+        raise KDAError(st, what)
     return workspace
 
 
@@ -170,36 +258,44 @@ def kda_chunk_state_pass(v, workspace, dk, S0=None, *, o=None, S_T=None, in_dtyp
                          out_dtype=torch.float32, want_state=True, stream=None):
     """Second stage of kda_chunk_fwd: the sequential pass from S0 over the chunks
     prepared in `workspace` (by kda_chunk_prep on the same sizes and in_dtype)."""
+    what = "kda_chunk_state_pass"
     lib = _load()
-    B, T, H, dv = v.shape
-    code = _dcode(v.dtype if in_dtype is None else in_dtype)
-    dev = v.device
+    B, T, H, dv = _dims(v, 4, what, "v")
+    in_dt = v.dtype if in_dtype is None else in_dtype
+    code = _dcode(in_dt)
+    dev = _check(what, [("v", v, (B, T, H, dv), (in_dt,), True),
+                        ("workspace", workspace, None, _U8, True),
+                        ("S0", S0, (B, H, dk, dv), _F32, False),
+                        ("o", o, (B, T, H, dv), _OUT, False),
+                        ("S_T", S_T, (B, H, dk, dv), _F32, False)])
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    wbytes = workspace.numel() * workspace.element_size()
-    st = lib.kda_chunk_state_pass(_ptr(v), _ptr(workspace), wbytes, _ptr(S0), _ptr(o), _ptr(S_T),
-                                  B, T, H, dk, dv, code, _dcode(o.dtype), _stream(stream, dev))
+    st = lib.kda_chunk_state_pass(_ptr(v), _ptr(workspace), _nbytes(workspace), _ptr(S0), _ptr(o),
+                                  _ptr(S_T), B, T, H, dk, dv, code, _dcode(o.dtype),
+                                  _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_chunk_state_pass")
+        raise KDAError(st, what)
     return o, S_T
+
+
+def _decode_specs(what, q, k, v, g, beta, S, o, out_dtype):
+    N, H, dk = _dims(q, 3, what, "q")
+    dv = _dims(v, 3, what, "v")[-1]
+    dt = _in_dtypes(q)
+    specs = [("q", q, (N, H, dk), dt, True), ("k", k, (N, H, dk), dt, True),
+             ("v", v, (N, H, dv), dt, True), ("g", g, (N, H, dk), dt, True),
+             ("beta", beta, (N, H), dt, True), ("S", S, (N, H, dk, dv), _F32, True),
+             ("o", o, (N, H, dv), _OUT, False)]
+    return (N, H, dk, dv), specs
 
 
 def kda_decode_step(q, k, v, g, beta, S, *, o=None, out_dtype=torch.float32, stream=None):
     """One decode step for N requests. q, k, g [N,H,dk]; v [N,H,dv]; beta [N,H];
     S [N,H,dk,dv] float32, updated in place. Returns o [N,H,dv]."""
-    lib = _load()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
-    if o is None:
-        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
-                             N, H, dk, dv, _dcode(q.dtype), _dcode(o.dtype),
-                             _stream(stream, q.device))
-    if st != _STATUS_OK:
-        raise KDAError(st, "kda_decode_step")
-    return o
+    return kda_decode_step_ex(q, k, v, g, beta, S, o=o, out_dtype=out_dtype, stream=stream,
+                              _what="kda_decode_step")
 
 
 def kda_chunk_fwd_ex(q, k, v, g, beta, S0=None, *, gate=KDA_GATE_LOG_DECAY, snapshot_every=0,
@@ -209,44 +305,43 @@ def kda_chunk_fwd_ex(q, k, v, g, beta, S0=None, *, gate=KDA_GATE_LOG_DECAY, snap
     and state snapshots every `snapshot_every` tokens (0: none) into
     `snapshots` [B, T // snapshot_every, H, dk, dv] float32 (allocated here
     when not given). Returns (o, S_T, snapshots or None)."""
+    what = "kda_chunk_fwd_ex"
     lib = _load()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    (B, T, H, dk, dv), specs = _fwd_specs(what, q, k, v, g, beta, S0, o, S_T, out_dtype)
+    nsnap = T // snapshot_every if snapshot_every > 0 else 0
+    specs.append(("snapshots", snapshots, (B, nsnap, H, dk, dv), _F32, False))
+    dev = _check(what, specs)
     code = _dcode(q.dtype)
-    dev = q.device
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    nsnap = T // snapshot_every if snapshot_every > 0 else 0
     if snapshots is None and nsnap > 0:
         snapshots = torch.empty((B, nsnap, H, dk, dv), dtype=torch.float32, device=dev)
     need = int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    workspace = _workspace(lib, what, workspace, need, dev)
     st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
                               _ptr(S_T), B, T, H, dk, dv, code, _dcode(o.dtype), int(gate),
-                              _ptr(snapshots), int(snapshot_every), _ptr(workspace), wbytes,
-                              _stream(stream, dev))
+                              _ptr(snapshots), int(snapshot_every), _ptr(workspace),
+                              _nbytes(workspace), _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_chunk_fwd_ex")
+        raise KDAError(st, what)
     return o, S_T, snapshots
 
 
 def kda_decode_step_ex(q, k, v, g, beta, S, *, gate=KDA_GATE_LOG_DECAY, o=None,
-                       out_dtype=torch.float32, stream=None):
+                       out_dtype=torch.float32, stream=None, _what="kda_decode_step_ex"):
     """kda_decode_step with a gate option. Returns o [N,H,dv]; S updated in place."""
     lib = _load()
-    N, H, dk = q.shape
-    dv = v.shape[-1]
+    (N, H, dk, dv), specs = _decode_specs(_what, q, k, v, g, beta, S, o, out_dtype)
+    dev = _check(_what, specs)
     if o is None:
-        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
                                 N, H, dk, dv, _dcode(q.dtype), _dcode(o.dtype), int(gate),
-                                _stream(stream, q.device))
+                                _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_decode_step_ex")
+        raise KDAError(st, _what)
     return o
 
 
@@ -255,29 +350,39 @@ def kda_spec_verify(q, k, v, g, beta, S, *, gate=KDA_GATE_LOG_DECAY, o=None,
     """Outputs of T draft tokens per request from the checkpoint S (read only).
     q, k, g [N,T,H,dk]; v [N,T,H,dv]; beta [N,T,H]; S [N,H,dk,dv] float32.
     Returns o [N,T,H,dv]."""
+    what = "kda_spec_verify"
     lib = _load()
-    N, T, H, dk = q.shape
-    dv = v.shape[-1]
+    N, T, H, dk = _dims(q, 4, what, "q")
+    dv = _dims(v, 4, what, "v")[-1]
+    dt = _in_dtypes(q)
+    dev = _check(what, [("q", q, (N, T, H, dk), dt, True), ("k", k, (N, T, H, dk), dt, True),
+                        ("v", v, (N, T, H, dv), dt, True), ("g", g, (N, T, H, dk), dt, True),
+                        ("beta", beta, (N, T, H), dt, True), ("S", S, (N, H, dk, dv), _F32, True),
+                        ("o", o, (N, T, H, dv), _OUT, False)])
     if o is None:
-        o = torch.empty((N, T, H, dv), dtype=out_dtype, device=q.device)
+        o = torch.empty((N, T, H, dv), dtype=out_dtype, device=dev)
     st = lib.kda_spec_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
                              N, T, H, dk, dv, _dcode(q.dtype), _dcode(o.dtype), int(gate),
-                             _stream(stream, q.device))
+                             _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_spec_verify")
+        raise KDAError(st, what)
     return o
 
 
 def kda_spec_commit(k, v, g, beta, S, accepted, *, gate=KDA_GATE_LOG_DECAY, stream=None):
     """Advance the checkpoint S [N,H,dk,dv] in place over the first accepted[n]
     (int32 [N] on the device) of the T logged tokens. Returns S."""
+    what = "kda_spec_commit"
     lib = _load()
-    N, T, H, dk = k.shape
-    dv = v.shape[-1]
-    if accepted.dtype != torch.int32:
-        raise TypeError("accepted must be int32")
+    N, T, H, dk = _dims(k, 4, what, "k")
+    dv = _dims(v, 4, what, "v")[-1]
+    dt = _in_dtypes(k)
+    dev = _check(what, [("k", k, (N, T, H, dk), dt, True), ("v", v, (N, T, H, dv), dt, True),
+                        ("g", g, (N, T, H, dk), dt, True), ("beta", beta, (N, T, H), dt, True),
+                        ("S", S, (N, H, dk, dv), _F32, True),
+                        ("accepted", accepted, (N,), (torch.int32,), True)])
     st = lib.kda_spec_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(accepted),
-                             N, T, H, dk, dv, _dcode(k.dtype), int(gate), _stream(stream, k.device))
+                             N, T, H, dk, dv, _dcode(k.dtype), int(gate), _stream(stream, dev))
     if st != _STATUS_OK:
-        raise KDAError(st, "kda_spec_commit")
+        raise KDAError(st, what)
     return S

@@ -105,20 +105,25 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
  *   workspace, workspace_bytes: device scratch of at least
  *            kda_chunk_fwd_workspace_size(...) bytes, owned by the caller,
  *            not read before it is written; contents after the call are
- *            unspecified. Must not overlap any tensor.
+ *            unspecified. Must not overlap any tensor. Calls that run at
+ *            the same time must not share a workspace.
  *
  * Supported: dk in {64, 128}; dv a multiple of 16 in [16, 512]; B, H >= 0
  * with H * dv <= 2^25;
  * T >= 0 (T = 0 copies S0, or zeros, into S_T). in_dtype KDA_F32 (all fp32
  * arithmetic, fp32 matrix-core products) or KDA_BF16 (bf16 inputs; bf16
- * split-precision chunk Gram products, fp16 state products, fp32
- * accumulation and fp32 state); out_dtype KDA_F32 or KDA_BF16.
+ * split-precision chunk Gram products, fp16 state and update products, v
+ * exact in bf16 products, fp32 accumulation and fp32 state); out_dtype
+ * KDA_F32 or KDA_BF16.
  * The computation works in chunks of 16 tokens aligned at t = 0; a last
  * partial chunk is padded internally with tokens that leave S unchanged.
  * With KDA_BF16 inputs the sequential pass advances two chunks (32 tokens)
- * per step.
- * With KDA_BF16 inputs, entries of v, of the state and of the per-chunk
- * update (beta times prediction error) must stay below 65504 in magnitude.
+ * per step. Values of v, S0, the state and the per-chunk update have no
+ * range limit beyond fp32's: a slice whose state would leave the fp16
+ * operand range (or fall far below it) is recomputed with an exact
+ * power-of-two scale. The precomputed per-chunk operands are held in fp16;
+ * they are at most 1 in magnitude for queries and keys of norm at most 1
+ * (the method's L2-normalised q and k) and beta in [0, 1].
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const float* S0, void* o, float* S_T,
@@ -155,7 +160,10 @@ kda_status kda_chunk_fwd_check(const void* q, const void* k, const void* v,
  *
  * kda_chunk_state_pass: the sequential pass over the chunks of each (b, h)
  * from S0, reading v and the workspace written by kda_chunk_prep for the same
- * B, T, H, dk, dv and in_dtype; writes o and S_T.
+ * B, T, H, dk, dv and in_dtype; writes o and S_T. With KDA_BF16 inputs it
+ * also writes a few bytes of the workspace past the prepared operands (one
+ * flag per 16-column slice of the state), so two state passes over one
+ * workspace must not run at the same time.
  */
 kda_status kda_chunk_prep(const void* q, const void* k, const void* g, const void* beta,
                           int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,

@@ -53,11 +53,15 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
   if (dv < 16 || dv > 512 || dv % 16 != 0) return 0;
   if (B > kMaxElems || T > kMaxElems || H > kMaxElems) return 0;
   // fp32 inputs: one record per 16-token chunk; bf16 inputs: one per pair
+  // of chunks, then one int per (b, h, 16-column slice) for the state pass
+  // (whole KiB)
   const int64_t units = in_dtype == KDA_F32 ? (T + 15) / 16 : (T + 31) / 32;
   const int64_t bytes = in_dtype == KDA_F32 ? kda::record_layout(dk).bytes : kda::pair_layout(dk).bytes;
   const double total = static_cast<double>(B) * H * units * bytes;
   if (total > 9.0e18) return 0;
-  return static_cast<size_t>(B * H * units * bytes);
+  if (units == 0 || B * H == 0) return 0;
+  const int64_t flags = in_dtype == KDA_F32 ? 0 : (B * H * (dv / 16) * 4 + 1023) / 1024 * 1024;
+  return static_cast<size_t>(B * H * units * bytes + flags);
 }
 
 }  // extern "C"

@@ -50,6 +50,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename InT>
 constexpr bool kIsF32 = std::is_same<InT, float>::value;
 
+// Four fp32 values as bf16 [high parts | low parts]: x = hi + lo to about 16
+// bits. A 16-deep contraction against an exact bf16 operand repeated in both
+// halves then costs one 32-deep matrix-core product.
+__device__ __forceinline__ bf16x8 split_bf16(const float (&x)[4]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = static_cast<__bf16>(x[i]);
+    r[i + 4] = static_cast<__bf16>(x[i] - static_cast<float>(r[i]));
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Record fragment addressing. Each lane's values come in groups of 4
 // consecutive rows/tokens i = 0..3.
@@ -60,11 +73,12 @@ constexpr bool kIsF32 = std::is_same<InT, float>::value;
 //   eg:   e^gamma[channel 16m + 4gq + i] at float index gq*dk/4 + 4m + i
 // Per-chunk record (fp32 inputs, RecordLayout): W, Q, Kb as 4 floats at
 // ((m*64 + l) * 16); M, Tb at l*16.
-// Pair record (bf16 inputs, PairLayout; fp16 operands): W, Q packed per pair
-// of tiles (2p, 2p+1) as 8 halves (16 B) at ((p*64 + l) * 16); Kb of both
-// chunks as 8 halves at ((m*64 + l) * 16), chunk 1 in the low four; the
-// 16x16 tiles as 8 halves at l*16 (two tiles side by side, or a high and a
-// low part); Tb of chunk 1 as 4 halves at l*8.
+// Pair record (bf16 inputs, PairLayout): W, Q packed per pair of tiles
+// (2p, 2p+1) as 8 fp16 halves (16 B) at ((p*64 + l) * 16); Kb of both chunks
+// as 8 halves at ((m*64 + l) * 16), chunk 1 in the low four; the M tiles as 8
+// halves at l*16 (two tiles side by side, or a high and a low part); Tb of
+// each chunk as 8 bf16 at l*16 (high parts, then low parts); -C21 as 4 halves
+// at l*8.
 // ---------------------------------------------------------------------------
 
 // Chunk prep for fp32 inputs: one wavefront per (b, h, chunk), fp32 matrix
@@ -418,15 +432,13 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
       *reinterpret_cast<f16x4*>(rec + L.kb + static_cast<size_t>(m * 64 + l) * 16) = kv;
     }
     f16x8 mm;
-    f16x4 tv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       mm[i] = static_cast<Op>(mf[i]);
       mm[i + 4] = static_cast<Op>(mf[i] - static_cast<float>(mm[i]));
-      tv[i] = static_cast<Op>(tb[i]);
     }
     *reinterpret_cast<f16x8*>(rec + L.m1 + static_cast<size_t>(l) * 16) = mm;
-    *reinterpret_cast<f16x4*>(rec + L.tb1 + static_cast<size_t>(l) * 8) = tv;
+    *reinterpret_cast<bf16x8*>(rec + L.tb1 + static_cast<size_t>(l) * 16) = split_bf16(tb);
   } else {
     // ---- coupling tiles from Kb1 (wavefront 0's, in LDS): lane gets
     // C21[c16][4gq + i] and M21[c16][4gq + i] (products with Kb1 as the
@@ -469,7 +481,8 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
       for (int i = 0; i < 4; ++i) kv[i] = s_kb[1][(4 * gq + i) * LDK + 16 * m + c16];
       *reinterpret_cast<f16x4*>(rec + L.kb + static_cast<size_t>(m * 64 + l) * 16 + 8) = kv;
     }
-    f16x8 mh, ml, tc;
+    f16x8 mh, ml;
+    f16x4 cv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const Op a = static_cast<Op>(M21T[i]), c = static_cast<Op>(mf[i]);
@@ -477,12 +490,12 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
       ml[i] = static_cast<Op>(M21T[i] - static_cast<float>(a));
       mh[i + 4] = c;
       ml[i + 4] = static_cast<Op>(mf[i] - static_cast<float>(c));
-      tc[i] = static_cast<Op>(tb[i]);
-      tc[i + 4] = static_cast<Op>(-C21T[i]);
+      cv[i] = static_cast<Op>(-C21T[i]);
     }
     *reinterpret_cast<f16x8*>(rec + L.m2h + static_cast<size_t>(l) * 16) = mh;
     *reinterpret_cast<f16x8*>(rec + L.m2l + static_cast<size_t>(l) * 16) = ml;
-    *reinterpret_cast<f16x8*>(rec + L.tc2 + static_cast<size_t>(l) * 16) = tc;
+    *reinterpret_cast<bf16x8*>(rec + L.tb2 + static_cast<size_t>(l) * 16) = split_bf16(tb);
+    *reinterpret_cast<f16x4*>(rec + L.c21 + static_cast<size_t>(l) * 8) = cv;
     if (c16 == 15) {  // e^(gamma1 + gamma2), laid out as eg of kda_chunk_prep
       float* egp = reinterpret_cast<float*>(rec + L.eg) + gq * (DK / 4);
 #pragma unroll
@@ -741,9 +754,45 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Power-of-two scale of the bf16 path's state pass (see the compute wave):
+// the slice's largest magnitude is kept in [kScaleLow, kScaleHigh], far
+// inside the fp16 range ([2^-14, 65504] normal), with |e| <= kScaleMax.
+constexpr float kScaleHigh = 16384.f;     // 2^14: fp16 holds 4x more
+constexpr float kScaleLow = 0.0625f;      // 2^-4
+constexpr int kScaleMax = 120;
+
+// 2^x for an integer x in [-126, 127], exact.
+__device__ __forceinline__ float pow2f(int x) { return __int_as_float((127 + x) << 23); }
+
+// Largest value over the 64 lanes of the wavefront.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// Largest magnitude in this lane's state slice, as a shallow tree of
+// three-input maxima with absolute-value operands (NaN is ignored by the max).
+template <int NM>
+__device__ __forceinline__ float state_max(const f32x4 (&S)[NM]) {
+  float part[NM];
+#pragma unroll
+  for (int k = 0; k < NM; ++k)
+    part[k] = fmaxf(fmaxf(fmaxf(fabsf(S[k][0]), fabsf(S[k][1])), fabsf(S[k][2])), fabsf(S[k][3]));
+#pragma unroll
+  for (int w = 1; w < NM; w *= 2)
+#pragma unroll
+    for (int k = 0; k + w < NM; k += 2 * w) part[k] = fmaxf(part[k], part[k + w]);
+  return part[0];
+}
+
+__device__ __forceinline__ float tile_max(float m, const f32x4& U) {
+  return fmaxf(fmaxf(fmaxf(fmaxf(m, fabsf(U[0])), fabsf(U[1])), fabsf(U[2])), fabsf(U[3]));
+}
+
 template <int DK, int SPW>
 struct Ring32Geom {
-  static constexpr int kRec = DK == 128 ? 29696 : 17408;  // pair record bytes (pair_layout)
+  static constexpr int kRec = DK == 128 ? 30720 : 18432;  // pair record bytes (pair_layout)
   static constexpr int kUnits = kRec / 1024;              // 16-byte record loads per lane
   // + two V^T tiles (16 columns x 16 tokens fp16) per slice of the workgroup,
   // rows padded to 10 dwords so that the loader's transposing writes hit 64
@@ -785,8 +834,10 @@ struct PairFrags {
   static constexpr int NM = DK / 16;
   f16x8 w1[NM / 2], w2[NM / 2], q1[NM / 2], q2[NM / 2];
   f16x8 kb[NM];
-  f16x8 m1, m2h, m2l, tc2;
-  f16x4 tb1, v1, v2;
+  f16x8 m1, m2h, m2l;
+  bf16x8 tb1, tb2;
+  f16x4 c21;
+  bf16x4 v1, v2;
   f32x4 eg[NM];
 
   // vt: this slice's two V^T tiles (rows of kVPitch bytes, kVTile apart)
@@ -810,11 +861,12 @@ struct PairFrags {
     m1 = ld_at<f16x8>(slot + L.m1, lo);
     m2h = ld_at<f16x8>(slot + L.m2h, lo);
     m2l = ld_at<f16x8>(slot + L.m2l, lo);
-    tc2 = ld_at<f16x8>(slot + L.tc2, lo);
-    tb1 = ld_at<f16x4>(slot + L.tb1, static_cast<uint32_t>(l) * 8);
+    tb1 = ld_at<bf16x8>(slot + L.tb1, lo);
+    tb2 = ld_at<bf16x8>(slot + L.tb2, lo);
+    c21 = ld_at<f16x4>(slot + L.c21, static_cast<uint32_t>(l) * 8);
     const uint32_t vo = static_cast<uint32_t>(c16 * kVPitch + 8 * gq);
-    v1 = ld_at<f16x4>(vt, vo);
-    v2 = ld_at<f16x4>(vt + kVTile, vo);
+    v1 = ld_at<bf16x4>(vt, vo);
+    v2 = ld_at<bf16x4>(vt + kVTile, vo);
   }
 };
 
@@ -823,11 +875,17 @@ struct PairFrags {
 // shared ring, and the V loader loads every slice's V tiles. A compute unit
 // then advances SPW slices at once, for workloads with more slices than
 // compute units.
-template <typename OutT, int DK, int SPW>
+//
+// flags: one int per (b, h, slice), in the workspace after the records. The
+// plain pass (SCALED = false) writes every slice's flag; the scaled pass
+// (SCALED = true, SPW = 1) runs only the slices whose flag is set.
+template <typename OutT, int DK, int SPW, bool SCALED>
 __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kda_state_pass_ring32(
     const uint16_t* __restrict__ v, const uint8_t* __restrict__ ws, const float* S0,
     OutT* __restrict__ o, float* ST, float* __restrict__ snap, int64_t snap_pairs, int64_t T,
-    int64_t H, int64_t DV, int64_t NPR, int64_t ngroups, int64_t nheads, PairLayout L) {
+    int64_t H, int64_t DV, int64_t NPR, int64_t ngroups, int64_t nheads, PairLayout L,
+    int* __restrict__ flags) {
+  static_assert(!SCALED || SPW == 1, "the scaled pass serves one slice per workgroup");
   using G = Ring32Geom<DK, SPW>;
   constexpr int NM = DK / 16;
   constexpr int kR = G::kSlots, kS = G::kStages;
@@ -841,6 +899,9 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   const int64_t head = xcd + 8 * (kk / ngroups);
   const int64_t group = kk % ngroups;
   if (head >= nheads) return;  // whole workgroup
+  if constexpr (SCALED) {
+    if (flags[head * (DV / 16) + group] == 0) return;  // whole workgroup
+  }
   const int64_t b = head / H, h = head % H;
   const uint8_t* rec0 = ws + static_cast<size_t>(head) * NPR * G::kRec;
   const size_t hb = static_cast<size_t>(b * T * H + h) * DV;
@@ -893,10 +954,11 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
         if (j < G::kUnits) st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[u]);
       }
       if (has_v) {
-        // V^T[col][token] in fp16, one tile per chunk of the pair (rows of
-        // G::kVPitch bytes), two tiles per slice: the compute lane (c16, gq)
-        // reads tokens 4gq .. 4gq+3 of column c16. This lane writes tokens
-        // 2a, 2a + 1 of its four columns of each slice, one dword each.
+        // V^T[col][token], the exact bf16 values, one tile per chunk of the
+        // pair (rows of G::kVPitch bytes), two tiles per slice: the compute
+        // lane (c16, gq) reads tokens 4gq .. 4gq+3 of column c16. This lane
+        // writes tokens 2a, 2a + 1 of its four columns of each slice, one
+        // dword (two bf16) each.
 #pragma unroll
         for (int z = 0; z < SPW; ++z) {
           uint8_t* vt = dst + G::kRec + (2 * z + (va >> 3)) * G::kVTile + (va & 7) * 4;
@@ -904,12 +966,9 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
           const uint32_t r1[2] = {st.ok1 ? st.v1[z][0] : 0u, st.ok1 ? st.v1[z][1] : 0u};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const uint32_t b0 = (c & 1) ? (r0[c >> 1] & 0xffff0000u) : (r0[c >> 1] << 16);
+            const uint32_t b0 = (c & 1) ? (r0[c >> 1] >> 16) : (r0[c >> 1] & 0xffffu);
             const uint32_t b1 = (c & 1) ? (r1[c >> 1] & 0xffff0000u) : (r1[c >> 1] << 16);
-            f16x2 hv;
-            hv[0] = static_cast<_Float16>(__uint_as_float(b0));
-            hv[1] = static_cast<_Float16>(__uint_as_float(b1));
-            *reinterpret_cast<f16x2*>(vt + (4 * cq + c) * G::kVPitch) = hv;
+            *reinterpret_cast<uint32_t*>(vt + (4 * cq + c) * G::kVPitch) = b0 | b1;
           }
         }
       }
@@ -941,72 +1000,165 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   const int z = wave - kLd;  // this wavefront's slice within the group
   const int64_t slice = group * SPW + z;
   const int64_t col = slice * 16 + c16;
-  f32x4 S[NM];
   const size_t sbase = static_cast<size_t>(head) * DK * DV + col;
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
   OutT* ob = o + hb;
   // outputs in transposed fragments: lane (c16, gq) holds token c16 of the
   // chunk, value columns slice*16 + 4gq .. +3
   const uint32_t obt =
       static_cast<uint32_t>(c16 * H * DV + slice * 16 + 4 * gq) * static_cast<uint32_t>(sizeof(OutT));
   const size_t chunk_elems = pair_elems / 2;
-  int64_t next_snap = snap_pairs;
   float* snap_b = nullptr;
   if (snap_pairs > 0) {
     const int64_t ns = NPF / snap_pairs;
-    snap_b = snap + (static_cast<size_t>(b * ns) * H + h) * DK * DV + col;
+    snap_b = snap + (static_cast<size_t>(b * ns) * H + h) * DK * DV + slice * 16;
   }
+  // the slice in [dk, DV] row-major fp32 at a uniform base: per-lane byte
+  // offsets of rows 4gq + i of channel group 0 (DK * DV * 4 < 2^32)
+  const uint32_t srow = static_cast<uint32_t>(DV) * 4u;
+  const uint32_t slane = static_cast<uint32_t>(4 * gq) * srow + static_cast<uint32_t>(c16) * 4u;
+
+  // The state and update products take fp16 operands, so the state S and
+  // the update U must stay inside the fp16 range; v enters exact (bf16)
+  // through Tb V in fp32. The plain pass (SCALED = false) runs as is. A
+  // value past the fp16 range becomes an infinity there, and from then on
+  // the state holds a non-finite entry for good (the decay and the products
+  // keep infinities and NaN); values far below the range (all of |S| <
+  // kScaleLow at the end) lose fp16 precision. Either way the final state
+  // shows it: the plain pass then leaves S_T unwritten (so an in-place S0
+  // survives) and raises the slice's flag, and the scaled pass
+  // (SCALED = true, launched after it) redoes exactly the flagged slices
+  // from S0. Ordinary inputs pay one check per slice; NaN or infinite
+  // inputs run twice, with the same result.
+  //
+  // Scaled pass: the slice is held as S * 2^-e (fp32) with a wave-uniform
+  // integer e, and every step checks the largest |S 2^-e| and |U 2^-e|
+  // before the update products use them. Above kScaleHigh, or below
+  // kScaleLow in every lane, e moves so that the slice's largest magnitude
+  // lands in [2^5, 2^6) and the step's state products are redone. Powers of
+  // two scale exactly; while e = 0 the arithmetic is that of the plain pass.
+  f32x4 S[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+  int e = 0;
+  float dn = 1.f, up = 1.f;  // 2^-e, 2^e
+  int64_t next_snap = snap_pairs;
+  auto store_slice = [&](float* base) __attribute__((always_inline)) {
+    // an opaque copy keeps the 32 address computations inside this rare path
+    // (hoisted out of the loop they stay live for the whole sequence)
+    uint32_t lane_off = slane;
+    asm volatile("" : "+v"(lane_off));
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_at<float>(base, lane_off + (16 * m + i) * srow, S[m][i] * up);
+  };
   ring_barrier();
   for (int64_t n = 0; n < NPR; ++n) {
     PairFrags<DK> f;
     const uint8_t* slot = ring + static_cast<int>(n % kR) * G::kSlot;
     f.template load<G::kVPitch, G::kVTile>(slot, slot + G::kRec + 2 * z * G::kVTile, L, l, gq, c16);
-    f16x8 sh[NM / 2];
-#pragma unroll
-    for (int p = 0; p < NM / 2; ++p)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
-    f16x8 tbz, vz;
+    // Tb V of both chunks: v exact in bf16 (repeated in both halves of the
+    // contraction) against Tb's high and low bf16 parts
+    bf16x8 vv1, vv2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      tbz[i] = f.tb1[i];
-      tbz[i + 4] = static_cast<_Float16>(0.f);
-      vz[i] = f.v1[i];
-      vz[i + 4] = static_cast<_Float16>(0.f);
+      vv1[i] = vv1[i + 4] = f.v1[i];
+      vv2[i] = vv2[i + 4] = f.v2[i];
     }
-    f32x4 U1 = mma_16x16x32_f16(tbz, vz, zero4());               // Tb1 V1
-    f32x4 U2 = zero4(), O1 = zero4(), O2 = zero4();
+    const f32x4 TV1 = mma_16x16x32_bf16(f.tb1, vv1, zero4());
+    const f32x4 TV2 = mma_16x16x32_bf16(f.tb2, vv2, zero4());
+    f16x8 cz;
 #pragma unroll
-    for (int p = 0; p < NM / 2; ++p) {
-      U1 = mma_16x16x32_f16(f.w1[p], sh[p], U1);                  // - W1 S0
-      U2 = mma_16x16x32_f16(f.w2[p], sh[p], U2);                  // - W2 e^g1 S0
-      O1 = mma_16x16x32_f16(sh[p], f.q1[p], O1);                  // (Qt1 S0)^T
-      O2 = mma_16x16x32_f16(sh[p], f.q2[p], O2);                  // (Qt2 e^g1 S0)^T
+    for (int i = 0; i < 4; ++i) {
+      cz[i] = f.c21[i];
+      cz[i + 4] = static_cast<_Float16>(0.f);
     }
-    f16x8 u11, vu, u12;
+    f16x8 sh[NM / 2];
+    f32x4 U1, U2, O1, O2;
+    float mx = 0.f;
+    // the products that read the state: U1, U2 and the state parts of O1, O2
+    auto state_products = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < NM / 2; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sh[p][j] = static_cast<_Float16>(S[2 * p + (j >> 2)][j & 3]);
+      float ms = 0.f;
+      if constexpr (SCALED) ms = state_max(S);  // independent of the products below
+      U1 = TV1 * dn;                                              // Tb1 V1
+      U2 = TV2 * dn;                                              // Tb2 V2
+      O1 = zero4();
+      O2 = zero4();
+#pragma unroll
+      for (int p = 0; p < NM / 2; ++p) {
+        U1 = mma_16x16x32_f16(f.w1[p], sh[p], U1);                // - W1 S0
+        U2 = mma_16x16x32_f16(f.w2[p], sh[p], U2);                // - W2 e^g1 S0
+        O1 = mma_16x16x32_f16(sh[p], f.q1[p], O1);                // (Qt1 S0)^T
+        O2 = mma_16x16x32_f16(sh[p], f.q2[p], O2);                // (Qt2 e^g1 S0)^T
+      }
+      f16x8 uz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uz[i] = static_cast<_Float16>(U1[i]);
+        uz[i + 4] = static_cast<_Float16>(0.f);
+      }
+      U2 = mma_16x16x32_f16(cz, uz, U2);                          // - C21 U1
+      if constexpr (SCALED) mx = tile_max(tile_max(ms, U1), U2);
+    };
+    // NaN never counts (the max ignores it) and an infinite value does not
+    // either: both propagate unscaled
+    auto out_of_range = [&]() __attribute__((always_inline)) {
+      const float fin = mx <= 3.4028235e38f ? mx : 0.f;
+      return __any(fin > kScaleHigh) || (!__any(mx >= kScaleLow) && __any(fin > 0.f));
+    };
+    state_products();
+    if constexpr (SCALED) {
+      if (out_of_range()) {
+        // shift so that the slice's largest finite magnitude is in
+        // [2^5, 2^6), then redo the products (a branch, not a loop around
+        // the common path: a loop there makes the compiler wait for every
+        // fragment read before the first product)
+        for (int redo = 0; redo < 3; ++redo) {
+          const float fin = mx <= 3.4028235e38f ? mx : 0.f;
+          const int x = __builtin_amdgcn_frexp_expf(wave_max(fin));
+          int en = e - (6 - x);
+          en = en < -kScaleMax ? -kScaleMax : (en > kScaleMax ? kScaleMax : en);
+          const int d = __builtin_amdgcn_readfirstlane(e - en);
+          if (d == 0) break;  // held at the limit
+          e -= d;
+          dn = pow2f(-e);
+          up = pow2f(e);
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[m][i] = __builtin_amdgcn_ldexpf(S[m][i], d);
+          state_products();
+          if (!out_of_range()) break;
+        }
+      }
+    }
+    f16x8 u11, u12;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const _Float16 x = static_cast<_Float16>(U1[i]);
       u11[i] = x;
       u11[i + 4] = x;
-      vu[i] = f.v2[i];
-      vu[i + 4] = x;
       u12[i] = x;
+      u12[i + 4] = static_cast<_Float16>(U2[i]);
     }
-    U2 = mma_16x16x32_f16(f.tc2, vu, U2);                         // + Tb2 V2 - C21 U1
     O1 = mma_16x16x32_f16(u11, f.m1, O1);                         // + (M1 U1)^T
-#pragma unroll
-    for (int i = 0; i < 4; ++i) u12[i + 4] = static_cast<_Float16>(U2[i]);
     O2 = mma_16x16x32_f16(u12, f.m2h, O2);                        // + ([M21 | M2] [U1; U2])^T
     O2 = mma_16x16x32_f16(u12, f.m2l, O2);
     // S = Diag(e^(g1+g2)) S + [Kb1 e^g2 | Kb2]^T [U1; U2] (accumulator input
     // is the VALU product)
 #pragma unroll
     for (int m = 0; m < NM; ++m) S[m] = mma_16x16x32_f16(f.kb[m], u12, S[m] * f.eg[m]);
+    if constexpr (SCALED) {
+      O1 *= up;
+      O2 *= up;
+    }
     OutT* oc = ob + static_cast<size_t>(n) * pair_elems;
     if (n < NPF) {
       st_out4_at(oc, obt, O1);
@@ -1016,22 +1168,25 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       if (n * 32 + 16 + c16 < T) st_out4_at(oc + chunk_elems, obt, O2);
     }
     if (n + 1 == next_snap && n < NPF) {
-      float* sp = snap_b + static_cast<size_t>(n / snap_pairs) * H * DK * DV;
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sp[static_cast<size_t>(16 * m + 4 * gq + i) * DV] = S[m][i];
+      store_slice(snap_b + static_cast<size_t>(n / snap_pairs) * H * DK * DV);
       next_snap += snap_pairs;
     }
     ring_barrier();
   }
   for (int64_t k = NPR; k < NPS; ++k) ring_barrier();  // match the loader's steps
-  if (ST) {
+  if constexpr (!SCALED) {
+    // suspect: a non-finite entry anywhere in the slice (the sum keeps it),
+    // or every entry below kScaleLow
+    float sum = 0.f;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ST[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] = S[m][i];
+      for (int i = 0; i < 4; ++i) sum += fabsf(S[m][i]);
+    const bool suspect = __any(!(sum <= 3.4028235e38f)) || !__any(state_max(S) >= kScaleLow);
+    if (l == 0) flags[head * (DV / 16) + slice] = suspect ? 1 : 0;
+    if (suspect) return;
   }
+  if (ST) store_slice(ST + static_cast<size_t>(head) * DK * DV + slice * 16);
 }
 
 // T = 0: the final state is the initial one (or zeros).
@@ -1071,7 +1226,7 @@ inline bool wants_snapshots(const ChunkFwdArgs& a) {
   return a.snapshots != nullptr && a.snapshot_every > 0 && a.T >= a.snapshot_every;
 }
 
-template <typename OutT, int DK, int SPW>
+template <typename OutT, int DK, int SPW, bool SCALED>
 hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t stream) {
   using G = Ring32Geom<DK, SPW>;
   const PairLayout P = pair_layout(DK);
@@ -1080,12 +1235,23 @@ hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t 
   const int64_t ngroups = a.dv / 16 / SPW;
   const int64_t nheads = a.B * a.H;
   const int64_t blocks = 8 * ngroups * ((nheads + 7) / 8);
-  hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK, SPW>), dim3(static_cast<uint32_t>(blocks)),
-                     dim3(64 * (G::kLoaders + SPW)), 0, stream, static_cast<const uint16_t*>(a.v),
-                     static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o), a.S_T,
-                     snap_pairs > 0 ? a.snapshots : nullptr, snap_pairs, a.T, a.H, a.dv, NPR, ngroups,
-                     nheads, P);
+  int* flags = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) +
+                                      static_cast<size_t>(nheads * NPR) * G::kRec);
+  hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK, SPW, SCALED>),
+                     dim3(static_cast<uint32_t>(blocks)), dim3(64 * (G::kLoaders + SPW)), 0, stream,
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint8_t*>(a.workspace),
+                     a.S0, static_cast<OutT*>(a.o), a.S_T, snap_pairs > 0 ? a.snapshots : nullptr,
+                     snap_pairs, a.T, a.H, a.dv, NPR, ngroups, nheads, P, flags);
   return hipGetLastError();
+}
+
+// The plain pass with SPW slices per workgroup, then the scaled pass over the
+// slices it flagged (one per workgroup; the others exit at once).
+template <typename OutT, int DK, int SPW>
+hipError_t launch_ring32_pair(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t stream) {
+  const hipError_t e = launch_ring32<OutT, DK, SPW, false>(a, snap_pairs, stream);
+  if (e != hipSuccess) return e;
+  return launch_ring32<OutT, DK, 1, true>(a, snap_pairs, stream);
 }
 
 // Slices per state-pass workgroup (1, 2 or 4, a divisor of the slice count).
@@ -1126,9 +1292,9 @@ hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidDevice;
     switch (choose_slices_per_wg(nheads, nslices, cus > 0 ? cus : 1)) {
-      case 4: return launch_ring32<OutT, DK, 4>(a, snap_pairs, stream);
-      case 2: return launch_ring32<OutT, DK, 2>(a, snap_pairs, stream);
-      default: return launch_ring32<OutT, DK, 1>(a, snap_pairs, stream);
+      case 4: return launch_ring32_pair<OutT, DK, 4>(a, snap_pairs, stream);
+      case 2: return launch_ring32_pair<OutT, DK, 2>(a, snap_pairs, stream);
+      default: return launch_ring32_pair<OutT, DK, 1>(a, snap_pairs, stream);
     }
   } else {
     const RecordLayout L = record_layout(DK);

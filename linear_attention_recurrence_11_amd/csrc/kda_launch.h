@@ -36,17 +36,19 @@ inline RecordLayout record_layout(int64_t dk) {
 
 // Per-(batch, head, pair of chunks) workspace record of the bf16-input path:
 // the state pass advances 32 tokens (two 16-token chunks c1, c2) per step.
-// All matrix-core operands are fp16, in fragment order (see kda_chunk.hip):
-//   w1, w2   -W of c1 and -W of c2 times Diag(e^gamma1)      (16 x dk each)
-//   q1, q2   Qt of c1 and Qt of c2 times Diag(e^gamma1)
-//   kb       [Kb of c1 times Diag(e^gamma2) | Kb of c2]      (dk x 32)
-//   m1       [M of c1, high | low parts]
+// Operands in fragment order (see kda_chunk.hip). The tiles that multiply
+// the state or the update are fp16; those that multiply v keep v exact in
+// bf16 and are split into bf16 high and low parts:
+//   w1, w2   -W of c1 and -W of c2 times Diag(e^gamma1)      (16 x dk each, fp16)
+//   q1, q2   Qt of c1 and Qt of c2 times Diag(e^gamma1)      (fp16)
+//   kb       [Kb of c1 times Diag(e^gamma2) | Kb of c2]      (dk x 32, fp16)
+//   m1       [M of c1, high | low parts]                      (fp16)
 //   m2h, m2l [M21 | M of c2], high and low parts, M21 = Qt2 Kb1^T
-//   tc2      [Tm beta of c2 | -C21], C21 = W2 Kb1^T
-//   tb1      Tm beta of c1
+//   tb1, tb2 Tm beta of c1 and of c2, [high | low] (bf16)
+//   c21      -C21, C21 = W2 Kb1^T                             (fp16)
 //   eg       e^(gamma1 + gamma2) per channel, fp32
 struct PairLayout {
-  int64_t w1, w2, q1, q2, kb, m1, m2h, m2l, tc2, tb1, eg, bytes;
+  int64_t w1, w2, q1, q2, kb, m1, m2h, m2l, tb1, tb2, c21, eg, bytes;
 };
 
 inline PairLayout pair_layout(int64_t dk) {
@@ -60,9 +62,10 @@ inline PairLayout pair_layout(int64_t dk) {
   L.m1 = 6 * tile;            // 64 lanes x 16 bytes each from here on
   L.m2h = L.m1 + 1024;
   L.m2l = L.m2h + 1024;
-  L.tc2 = L.m2l + 1024;
-  L.tb1 = L.tc2 + 1024;       // 64 lanes x 8 bytes
-  L.eg = L.tb1 + 512;
+  L.tb1 = L.m2l + 1024;
+  L.tb2 = L.tb1 + 1024;
+  L.c21 = L.tb2 + 1024;       // 64 lanes x 8 bytes
+  L.eg = L.c21 + 512;
   const int64_t end = L.eg + dk * 4;
   L.bytes = (end + 1023) / 1024 * 1024;  // whole 1 KiB units: 64 lanes x 16 bytes
   return L;

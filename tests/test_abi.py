@@ -46,10 +46,13 @@ def test_version_and_status_strings(lib):
 def test_workspace_size(lib):
     # fp32 inputs: one record per (b, h, 16-token chunk), whole KiB: 27648 B
     # (dk 128), 15360 B (dk 64); bf16 inputs: one per (b, h, pair of chunks):
-    # 29696 B (dk 128), 17408 B (dk 64)
-    assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == 32 * 2048 * 29696
-    assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == 64 * 128 * 29696
-    assert binding.kda_chunk_fwd_workspace_size(1, 33, 2, 64, 64, BF16) == 2 * 2 * 17408
+    # 30720 B (dk 128), 18432 B (dk 64), then a 4-byte flag per (b, h, 16-column
+    # slice), rounded up to whole KiB
+    assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == \
+        32 * 2048 * 30720 + 1024
+    assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == \
+        64 * 128 * 30720 + 2048
+    assert binding.kda_chunk_fwd_workspace_size(1, 33, 2, 64, 64, BF16) == 2 * 2 * 18432 + 1024
     assert binding.kda_chunk_fwd_workspace_size(1, 256, 2, 64, 64, F32) == 2 * 16 * 15360
     assert binding.kda_chunk_fwd_workspace_size(1, 17, 1, 128, 128, F32) == 2 * 27648
     assert binding.kda_chunk_fwd_workspace_size(1, 0, 1, 128, 128, F32) == 0

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -299,6 +299,59 @@ kda_status kda_spec_commit_check(const void* k, const void* v, const void* g,
                                  const void* beta, const float* S,
                                  const int32_t* accepted, int64_t N, int64_t T, int64_t H,
                                  int64_t dk, int64_t dv, int in_dtype, int gate);
+
+/*
+ * Context-parallel prefill, the part one device runs: a sequence cut into
+ * spans is prepared and passed span by span without knowing the state that
+ * enters each span, and the spans are joined afterwards (KDA context
+ * parallelism: "K3 tech report" podcast transcript, the exchange on
+ * recreating the training efficiency; "Kimi K3 goes trillion-scale with
+ * sparse MoE efficiency" subtitles, cue 22). The recurrence is affine in the
+ * state: a span maps its entering state S_in to F S_in + E, with F its state
+ * transition and E the state it reaches from zero.
+ *
+ * kda_chunk_transition: for the tokens of a workspace written by
+ * kda_chunk_prep (same B, T, H, dk, dv, in_dtype), the transition
+ *   F  [B, H, dk, dk] fp32, the state after the tokens from S_in = I with
+ *      v = 0 (NULL: not wanted)
+ * and the state from zero
+ *   E  [B, H, dk, dv] fp32, the state after the tokens from S_in = 0
+ *      (NULL: not wanted; v is then not read and may be NULL)
+ *   v  [B, T, H, dv] in_dtype, 16-byte aligned (needed for E only).
+ * F costs a state pass over dk columns that reads no v and writes no
+ * outputs (cheaper than kda_chunk_state_pass over an identity state and zero
+ * values, which writes T x H x dk outputs); E a state pass without outputs.
+ * T = 0 gives F = I, E = 0. F and E must not overlap each other, v or the
+ * workspace. Same sizes and rules as kda_chunk_fwd otherwise; the workspace
+ * is written past the prepared operands as by kda_chunk_state_pass.
+ *
+ * kda_state_affine_scan: the entering state of every span,
+ *   S[0] = S0,  S[r + 1] = F[r] S[r] + E[r],  r = 0 .. P-1,
+ * for N independent units (N = B * H):
+ *   F   [P, N, dk, dk] fp32, 16-byte aligned
+ *   E   [P, N, dk, dv] fp32
+ *   S0  [N, dk, dv]    fp32 (NULL means zeros)
+ *   S   [P + 1, N, dk, dv] fp32 out; S[P] is the state after the last span.
+ *       S must not overlap F, E or S0.
+ * Products in fp32 on the matrix cores, fp32 accumulation. dk in {64, 128};
+ * dv a multiple of 16 in [16, 512]; P, N >= 0.
+ */
+kda_status kda_chunk_transition(const void* v, const void* workspace, size_t workspace_bytes,
+                                float* F, float* E, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                int64_t dv, int in_dtype, void* stream);
+
+kda_status kda_state_affine_scan(const float* F, const float* E, const float* S0, float* S,
+                                 int64_t P, int64_t N, int64_t dk, int64_t dv, void* stream);
+
+/* Host-only checks of the two calls above (see kda_chunk_fwd_check). */
+kda_status kda_chunk_transition_check(const void* v, const void* workspace,
+                                      size_t workspace_bytes, const float* F, const float* E,
+                                      int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                      int in_dtype);
+
+kda_status kda_state_affine_scan_check(const float* F, const float* E, const float* S0,
+                                       const float* S, int64_t P, int64_t N, int64_t dk,
+                                       int64_t dv);
 
 #ifdef __cplusplus
 }

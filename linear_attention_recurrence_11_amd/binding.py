@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 # The argument lists below follow this version of include/kda.h.
-ABI_VERSION = 2
+ABI_VERSION = 3
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_LOG_DECAY, KDA_GATE_SIGMOID = 0, 1
 _STATUS_OK = 0
@@ -76,6 +76,14 @@ def _load():
         lib.kda_spec_commit.argtypes = [vp] * 6 + [i64] * 5 + [i, i, vp]
         lib.kda_spec_commit_check.restype = i
         lib.kda_spec_commit_check.argtypes = [vp] * 6 + [i64] * 5 + [i, i]
+        lib.kda_chunk_transition.restype = i
+        lib.kda_chunk_transition.argtypes = [vp, vp, sz, vp, vp] + [i64] * 5 + [i, vp]
+        lib.kda_chunk_transition_check.restype = i
+        lib.kda_chunk_transition_check.argtypes = [vp, vp, sz, vp, vp] + [i64] * 5 + [i]
+        lib.kda_state_affine_scan.restype = i
+        lib.kda_state_affine_scan.argtypes = [vp] * 4 + [i64] * 4 + [vp]
+        lib.kda_state_affine_scan_check.restype = i
+        lib.kda_state_affine_scan_check.argtypes = [vp] * 4 + [i64] * 4
         _LIB = lib
     return _LIB
 
@@ -383,6 +391,52 @@ def kda_spec_commit(k, v, g, beta, S, accepted, *, gate=KDA_GATE_LOG_DECAY, stre
                         ("accepted", accepted, (N,), (torch.int32,), True)])
     st = lib.kda_spec_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(accepted),
                              N, T, H, dk, dv, _dcode(k.dtype), int(gate), _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, what)
+    return S
+
+
+def kda_chunk_transition(workspace, B, T, H, dk, dv, in_dtype, *, v=None, F=None, E=None,
+                         want_F=True, want_E=False, stream=None):
+    """State transition F [B,H,dk,dk] and/or the state from zero E [B,H,dk,dv]
+    (needs v [B,T,H,dv]) of the tokens prepared in `workspace` by
+    kda_chunk_prep. Returns (F or None, E or None)."""
+    what = "kda_chunk_transition"
+    lib = _load()
+    in_dt = in_dtype if isinstance(in_dtype, torch.dtype) else (torch.float32, torch.bfloat16)[in_dtype]
+    code = _dcode(in_dt)
+    want_E = want_E or E is not None
+    want_F = want_F or F is not None
+    specs = [("workspace", workspace, None, _U8, True),
+             ("v", v, (B, T, H, dv), (in_dt,), want_E),
+             ("F", F, (B, H, dk, dk), _F32, False), ("E", E, (B, H, dk, dv), _F32, False)]
+    dev = _check(what, specs)
+    if F is None and want_F:
+        F = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    if E is None and want_E:
+        E = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    st = lib.kda_chunk_transition(_ptr(v), _ptr(workspace), _nbytes(workspace), _ptr(F), _ptr(E),
+                                  B, T, H, dk, dv, code, _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, what)
+    return F, E
+
+
+def kda_state_affine_scan(F, E, S0=None, *, S=None, stream=None):
+    """Entering states of P spans: S[0] = S0, S[r+1] = F[r] S[r] + E[r].
+    F [P,N,dk,dk], E [P,N,dk,dv], S0 [N,dk,dv] or None (zeros), all float32.
+    Returns S [P+1,N,dk,dv]."""
+    what = "kda_state_affine_scan"
+    lib = _load()
+    P, N, dk, _ = _dims(F, 4, what, "F")
+    dv = _dims(E, 4, what, "E")[-1]
+    dev = _check(what, [("F", F, (P, N, dk, dk), _F32, True), ("E", E, (P, N, dk, dv), _F32, True),
+                        ("S0", S0, (N, dk, dv), _F32, False),
+                        ("S", S, (P + 1, N, dk, dv), _F32, False)])
+    if S is None:
+        S = torch.empty((P + 1, N, dk, dv), dtype=torch.float32, device=dev)
+    st = lib.kda_state_affine_scan(_ptr(F), _ptr(E), _ptr(S0), _ptr(S), P, N, dk, dv,
+                                   _stream(stream, dev))
     if st != _STATUS_OK:
         raise KDAError(st, what)
     return S

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_decode.hip", "kda_spec.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_decode.hip", "kda_spec.hip", "kda_scan.hip"]
 ARCH = "gfx950"
 
 

@@ -60,7 +60,8 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
   const double total = static_cast<double>(B) * H * units * bytes;
   if (total > 9.0e18) return 0;
   if (units == 0 || B * H == 0) return 0;
-  const int64_t flags = in_dtype == KDA_F32 ? 0 : (B * H * (dv / 16) * 4 + 1023) / 1024 * 1024;
+  const int64_t cols = dk > dv ? dk : dv;  // the transition's passes run over dk columns
+  const int64_t flags = in_dtype == KDA_F32 ? 0 : (B * H * (cols / 16) * 4 + 1023) / 1024 * 1024;
   return static_cast<size_t>(B * H * units * bytes + flags);
 }
 
@@ -361,6 +362,100 @@ kda_status kda_spec_commit(const void* k, const void* v, const void* g, const vo
   kda::SpecArgs a{nullptr, k, v, g, beta, S, nullptr, accepted, N, T, H, dk, dv, in_dtype, KDA_F32};
   a.gate = gate;
   return launch_status(kda::launch_spec(a, true, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status check_transition(const void* v, const void* ws, size_t ws_bytes, const float* F,
+                            const float* E, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                            int in_dtype) {
+  if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return KDA_ERR_SHAPE;
+  if (B > kMaxElems || T > kMaxElems || H > kMaxElems) return KDA_ERR_SHAPE;
+  if (!dtype_ok(in_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (dk != 64 && dk != 128) return KDA_ERR_UNSUPPORTED;
+  if (dv < 16 || dv > 512 || dv % 16 != 0) return KDA_ERR_UNSUPPORTED;
+  const double toks = static_cast<double>(B) * T * H;
+  if (toks * (dk > dv ? dk : dv) > static_cast<double>(kMaxElems)) return KDA_ERR_SHAPE;
+  const int64_t NC = (T + 15) / 16;
+  if (B * H * NC > 0x7fffffffLL || B * H > 0x0fffffffLL) return KDA_ERR_UNSUPPORTED;
+  if (H * (dk > dv ? dk : dv) > (int64_t(1) << 25)) return KDA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if (BH == 0) return KDA_OK;
+  if (T > 0 && E && !v) return KDA_ERR_NULL;
+  const size_t need = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype);
+  if (T > 0 && (F || E) && (!ws || ws_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (T > 0 && E && !aligned(v, 16)) return KDA_ERR_ALIGNMENT;
+  if ((F && !aligned(F, 4)) || (E && !aligned(E, 4))) return KDA_ERR_ALIGNMENT;
+  if (T > 0 && (F || E) && !aligned(ws, 16)) return KDA_ERR_ALIGNMENT;
+  const Range none{0, 0};
+  const Range rv = T > 0 && E ? range_of(v, B * T * H * dv, dsize(in_dtype)) : none;
+  const Range rw = T > 0 && (F || E) ? range_of(ws, static_cast<int64_t>(need), 1) : none;
+  const Range rf = F ? range_of(F, BH * dk * dk, 4) : none;
+  const Range re = E ? range_of(E, BH * dk * dv, 4) : none;
+  if (overlap(rf, re) || overlap(rf, rv) || overlap(rf, rw) || overlap(re, rv) || overlap(re, rw))
+    return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status check_scan(const float* F, const float* E, const float* S0, const float* S, int64_t P,
+                      int64_t N, int64_t dk, int64_t dv) {
+  if (P < 0 || N < 0 || dk < 0 || dv < 0) return KDA_ERR_SHAPE;
+  if (dk != 64 && dk != 128) return KDA_ERR_UNSUPPORTED;
+  if (dv < 16 || dv > 512 || dv % 16 != 0) return KDA_ERR_UNSUPPORTED;
+  if (N > 0x0fffffffLL || P > 0x0fffffffLL ||
+      static_cast<double>(P + 1) * N * dk * (dk > dv ? dk : dv) > static_cast<double>(kMaxElems))
+    return KDA_ERR_SHAPE;
+  if (N == 0) return KDA_OK;
+  if (!S || (P > 0 && (!F || !E))) return KDA_ERR_NULL;
+  if (!aligned(S, 4) || (S0 && !aligned(S0, 4)) || (E && !aligned(E, 4))) return KDA_ERR_ALIGNMENT;
+  if (F && !aligned(F, 16)) return KDA_ERR_ALIGNMENT;  // read as 4-float vectors
+  const Range none{0, 0};
+  const Range rs = range_of(S, (P + 1) * N * dk * dv, 4);
+  const Range ins[] = {P > 0 ? range_of(F, P * N * dk * dk, 4) : none,
+                       P > 0 ? range_of(E, P * N * dk * dv, 4) : none,
+                       S0 ? range_of(S0, N * dk * dv, 4) : none};
+  for (const Range& x : ins)
+    if (overlap(rs, x)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_transition_check(const void* v, const void* workspace, size_t workspace_bytes,
+                                      const float* F, const float* E, int64_t B, int64_t T,
+                                      int64_t H, int64_t dk, int64_t dv, int in_dtype) {
+  return check_transition(v, workspace, workspace_bytes, F, E, B, T, H, dk, dv, in_dtype);
+}
+
+kda_status kda_chunk_transition(const void* v, const void* workspace, size_t workspace_bytes,
+                                float* F, float* E, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                int64_t dv, int in_dtype, void* stream) {
+  const kda_status st =
+      check_transition(v, workspace, workspace_bytes, F, E, B, T, H, dk, dv, in_dtype);
+  if (st != KDA_OK) return st;
+  if (B * H == 0 || (!F && !E)) return KDA_OK;
+  kda::ChunkFwdArgs a{nullptr, nullptr, v, nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H,
+                      dk, dv, in_dtype, KDA_F32, const_cast<void*>(workspace)};
+  return launch_status(kda::launch_chunk_transition(a, F, E, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_state_affine_scan_check(const float* F, const float* E, const float* S0,
+                                       const float* S, int64_t P, int64_t N, int64_t dk,
+                                       int64_t dv) {
+  return check_scan(F, E, S0, S, P, N, dk, dv);
+}
+
+kda_status kda_state_affine_scan(const float* F, const float* E, const float* S0, float* S,
+                                 int64_t P, int64_t N, int64_t dk, int64_t dv, void* stream) {
+  const kda_status st = check_scan(F, E, S0, S, P, N, dk, dv);
+  if (st != KDA_OK) return st;
+  if (N == 0) return KDA_OK;
+  return launch_status(
+      kda::launch_affine_scan(F, E, S0, S, P, N, dk, dv, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

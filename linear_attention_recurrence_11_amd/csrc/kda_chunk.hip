@@ -50,6 +50,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename InT>
 constexpr bool kIsF32 = std::is_same<InT, float>::value;
 
+// What a state pass computes: kPassOutputs, the forward (o, S_T);
+// kPassState, only the final state; kPassTransition, the state transition of
+// the tokens (each 16-column slice starts from its columns of the dk x dk
+// identity with v = 0, so S_T is the matrix F with S_out = F S_in + the
+// state reached from S_in = 0). The last two write no outputs.
+constexpr int kPassOutputs = 0, kPassState = 1, kPassTransition = 2;
+
 // Four fp32 values as bf16 [high parts | low parts]: x = hi + lo to about 16
 // bits. A 16-deep contraction against an exact bf16 operand repeated in both
 // halves then costs one 32-deep matrix-core product.
@@ -586,8 +593,8 @@ __device__ __forceinline__ f32x4 chunk_step(const ChunkFrags<DK>& cur, f32x4 (&S
 }
 
 // Sequential state pass for fp32 inputs: one wavefront per (b, h, 16-column
-// slice of dv), reading the per-chunk records.
-template <typename OutT, int DK>
+// slice of dv), reading the per-chunk records. MODE as for the bf16 pass.
+template <typename OutT, int DK, int MODE>
 __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v,
                                                      const uint8_t* __restrict__ ws,
                                                      const float* S0, OutT* __restrict__ o,
@@ -616,8 +623,13 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (MODE == kPassTransition)
+        S[m][i] = (16 * m + 4 * gq + i == col) ? 1.f : 0.f;
+      else
+        S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+    }
+  constexpr bool kOut = MODE == kPassOutputs;
 
   // Uniform per-(b,h) bases; per-lane offsets fixed for the whole sequence.
   const uint8_t* rec0 = ws + static_cast<size_t>(head) * NC * L.bytes;
@@ -643,7 +655,11 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
   auto fetch = [&](Frags& f, int64_t c) __attribute__((always_inline)) {
     c = c < NF - 1 ? c : NF - 1;
     f.load_record(rec0 + static_cast<size_t>(c) * L.bytes, L, l, gq);
-    f.load_v(vb + static_cast<size_t>(c) * chunk_elems, vbo);
+    if constexpr (MODE == kPassTransition) {
+      f.vv[0] = f.vv[1] = f.vv[2] = f.vv[3] = 0.f;
+    } else {
+      f.load_v(vb + static_cast<size_t>(c) * chunk_elems, vbo);
+    }
   };
   // Snapshots (snap_chunks > 0): the state after every snap_chunks full
   // chunks, i.e. after tokens [0, (j+1) * 16 * snap_chunks), goes to snapshot
@@ -660,6 +676,7 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
     snap_b = snap + (static_cast<size_t>(b * ns) * H + h) * DK * DV + col;
   }
   auto finish = [&](int64_t n, f32x4 O) __attribute__((always_inline)) {
+    if constexpr (!kOut) return;
     OutT* oc = ob + static_cast<size_t>(n) * chunk_elems;
 #pragma unroll
     for (int i = 0; i < 4; ++i) st_out_at(oc, obo[i], O[i]);
@@ -687,12 +704,18 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
     const int valid = static_cast<int>(T - NF * 16);
     Frags f;
     f.load_record(rec0 + static_cast<size_t>(NF) * L.bytes, L, l, gq);
-    f.load_v_partial(vb + static_cast<size_t>(NF) * chunk_elems, vbo, gq, valid);
+    if constexpr (MODE == kPassTransition) {
+      f.vv[0] = f.vv[1] = f.vv[2] = f.vv[3] = 0.f;
+    } else {
+      f.load_v_partial(vb + static_cast<size_t>(NF) * chunk_elems, vbo, gq, valid);
+    }
     const f32x4 O = chunk_step(f, S);
-    OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
+    if constexpr (kOut) {
+      OutT* oc = ob + static_cast<size_t>(NF) * chunk_elems;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
+      for (int i = 0; i < 4; ++i)
+        if (4 * gq + i < valid) st_out_at(oc, obo[i], O[i]);
+    }
   }
   if (ST) {
 #pragma unroll
@@ -879,7 +902,10 @@ struct PairFrags {
 // flags: one int per (b, h, slice), in the workspace after the records. The
 // plain pass (SCALED = false) writes every slice's flag; the scaled pass
 // (SCALED = true, SPW = 1) runs only the slices whose flag is set.
-template <typename OutT, int DK, int SPW, bool SCALED>
+//
+// MODE (kPassOutputs, kPassState or kPassTransition): the transition loads
+// no V; the two state-only modes skip the output products and stores.
+template <typename OutT, int DK, int SPW, bool SCALED, int MODE>
 __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kda_state_pass_ring32(
     const uint16_t* __restrict__ v, const uint8_t* __restrict__ ws, const float* S0,
     OutT* __restrict__ o, float* ST, float* __restrict__ snap, int64_t snap_pairs, int64_t T,
@@ -912,7 +938,7 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   constexpr int kLd = G::kLoaders;
   if (wave < kLd) {
     // ---------------- loaders ----------------
-    const bool has_v = wave == kLd - 1;
+    const bool has_v = wave == kLd - 1 && MODE != kPassTransition;
     // V: lane -> tokens 2a, 2a + 1 of the pair (a = 0..15), columns 4cq ..
     // 4cq + 3 of each slice of the group
     const int va = l & 15, cq = l >> 4;
@@ -1040,8 +1066,13 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (MODE == kPassTransition)
+        S[m][i] = (16 * m + 4 * gq + i == col) ? 1.f : 0.f;
+      else
+        S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
+    }
+  constexpr bool kOut = MODE == kPassOutputs;
   int e = 0;
   float dn = 1.f, up = 1.f;  // 2^-e, 2^e
   int64_t next_snap = snap_pairs;
@@ -1068,8 +1099,11 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       vv1[i] = vv1[i + 4] = f.v1[i];
       vv2[i] = vv2[i + 4] = f.v2[i];
     }
-    const f32x4 TV1 = mma_16x16x32_bf16(f.tb1, vv1, zero4());
-    const f32x4 TV2 = mma_16x16x32_bf16(f.tb2, vv2, zero4());
+    f32x4 TV1 = zero4(), TV2 = zero4();  // v = 0 for the transition
+    if constexpr (MODE != kPassTransition) {
+      TV1 = mma_16x16x32_bf16(f.tb1, vv1, zero4());
+      TV2 = mma_16x16x32_bf16(f.tb2, vv2, zero4());
+    }
     f16x8 cz;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1095,8 +1129,10 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       for (int p = 0; p < NM / 2; ++p) {
         U1 = mma_16x16x32_f16(f.w1[p], sh[p], U1);                // - W1 S0
         U2 = mma_16x16x32_f16(f.w2[p], sh[p], U2);                // - W2 e^g1 S0
-        O1 = mma_16x16x32_f16(sh[p], f.q1[p], O1);                // (Qt1 S0)^T
-        O2 = mma_16x16x32_f16(sh[p], f.q2[p], O2);                // (Qt2 e^g1 S0)^T
+        if constexpr (kOut) {
+          O1 = mma_16x16x32_f16(sh[p], f.q1[p], O1);              // (Qt1 S0)^T
+          O2 = mma_16x16x32_f16(sh[p], f.q2[p], O2);              // (Qt2 e^g1 S0)^T
+        }
       }
       f16x8 uz;
 #pragma unroll
@@ -1148,26 +1184,30 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       u12[i] = x;
       u12[i + 4] = static_cast<_Float16>(U2[i]);
     }
-    O1 = mma_16x16x32_f16(u11, f.m1, O1);                         // + (M1 U1)^T
-    O2 = mma_16x16x32_f16(u12, f.m2h, O2);                        // + ([M21 | M2] [U1; U2])^T
-    O2 = mma_16x16x32_f16(u12, f.m2l, O2);
+    if constexpr (kOut) {
+      O1 = mma_16x16x32_f16(u11, f.m1, O1);                       // + (M1 U1)^T
+      O2 = mma_16x16x32_f16(u12, f.m2h, O2);                      // + ([M21 | M2] [U1; U2])^T
+      O2 = mma_16x16x32_f16(u12, f.m2l, O2);
+    }
     // S = Diag(e^(g1+g2)) S + [Kb1 e^g2 | Kb2]^T [U1; U2] (accumulator input
     // is the VALU product)
 #pragma unroll
     for (int m = 0; m < NM; ++m) S[m] = mma_16x16x32_f16(f.kb[m], u12, S[m] * f.eg[m]);
-    if constexpr (SCALED) {
-      O1 *= up;
-      O2 *= up;
+    if constexpr (kOut) {
+      if constexpr (SCALED) {
+        O1 *= up;
+        O2 *= up;
+      }
+      OutT* oc = ob + static_cast<size_t>(n) * pair_elems;
+      if (n < NPF) {
+        st_out4_at(oc, obt, O1);
+        st_out4_at(oc + chunk_elems, obt, O2);
+      } else {  // last, partial pair: tokens past T are not stored
+        if (n * 32 + c16 < T) st_out4_at(oc, obt, O1);
+        if (n * 32 + 16 + c16 < T) st_out4_at(oc + chunk_elems, obt, O2);
+      }
     }
-    OutT* oc = ob + static_cast<size_t>(n) * pair_elems;
-    if (n < NPF) {
-      st_out4_at(oc, obt, O1);
-      st_out4_at(oc + chunk_elems, obt, O2);
-    } else {  // last, partial pair: tokens past T are not stored
-      if (n * 32 + c16 < T) st_out4_at(oc, obt, O1);
-      if (n * 32 + 16 + c16 < T) st_out4_at(oc + chunk_elems, obt, O2);
-    }
-    if (n + 1 == next_snap && n < NPF) {
+    if (kOut && n + 1 == next_snap && n < NPF) {
       store_slice(snap_b + static_cast<size_t>(n / snap_pairs) * H * DK * DV);
       next_snap += snap_pairs;
     }
@@ -1193,6 +1233,12 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
 __global__ void kda_copy_state(const float* S0, float* ST, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) ST[i] = S0 ? S0[i] : 0.f;
+}
+
+// The transition of an empty span: n / (d * d) identity matrices of d x d.
+__global__ void kda_identity_states(float* F, int64_t d, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) F[i] = (i % d) == ((i / d) % d) ? 1.f : 0.f;
 }
 
 template <typename InT, int DK, int GATE>
@@ -1226,7 +1272,7 @@ inline bool wants_snapshots(const ChunkFwdArgs& a) {
   return a.snapshots != nullptr && a.snapshot_every > 0 && a.T >= a.snapshot_every;
 }
 
-template <typename OutT, int DK, int SPW, bool SCALED>
+template <typename OutT, int DK, int SPW, bool SCALED, int MODE>
 hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t stream) {
   using G = Ring32Geom<DK, SPW>;
   const PairLayout P = pair_layout(DK);
@@ -1237,7 +1283,7 @@ hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t 
   const int64_t blocks = 8 * ngroups * ((nheads + 7) / 8);
   int* flags = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) +
                                       static_cast<size_t>(nheads * NPR) * G::kRec);
-  hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK, SPW, SCALED>),
+  hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK, SPW, SCALED, MODE>),
                      dim3(static_cast<uint32_t>(blocks)), dim3(64 * (G::kLoaders + SPW)), 0, stream,
                      static_cast<const uint16_t*>(a.v), static_cast<const uint8_t*>(a.workspace),
                      a.S0, static_cast<OutT*>(a.o), a.S_T, snap_pairs > 0 ? a.snapshots : nullptr,
@@ -1247,11 +1293,11 @@ hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t 
 
 // The plain pass with SPW slices per workgroup, then the scaled pass over the
 // slices it flagged (one per workgroup; the others exit at once).
-template <typename OutT, int DK, int SPW>
+template <typename OutT, int DK, int SPW, int MODE>
 hipError_t launch_ring32_pair(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t stream) {
-  const hipError_t e = launch_ring32<OutT, DK, SPW, false>(a, snap_pairs, stream);
+  const hipError_t e = launch_ring32<OutT, DK, SPW, false, MODE>(a, snap_pairs, stream);
   if (e != hipSuccess) return e;
-  return launch_ring32<OutT, DK, 1, true>(a, snap_pairs, stream);
+  return launch_ring32<OutT, DK, 1, true, MODE>(a, snap_pairs, stream);
 }
 
 // Slices per state-pass workgroup (1, 2 or 4, a divisor of the slice count).
@@ -1279,27 +1325,34 @@ inline int choose_slices_per_wg(int64_t nheads, int64_t nslices, int cus) {
   return best;
 }
 
-template <typename InT, typename OutT, int DK>
+// `a.dv` is the column count of the pass: the value dimension, or dk for
+// the transition.
+template <typename InT, typename OutT, int DK, int MODE>
 hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
   const int64_t nslices = a.dv / 16;
   const int64_t nheads = a.B * a.H;
   const int64_t blocks = 8 * nslices * ((nheads + 7) / 8);
-  const int64_t snap_chunks = wants_snapshots(a) ? a.snapshot_every / 16 : 0;
+  const int64_t snap_chunks =
+      MODE == kPassOutputs && wants_snapshots(a) ? a.snapshot_every / 16 : 0;
   if constexpr (!kIsF32<InT>) {  // bf16 inputs: 32 tokens per step
     const int64_t snap_pairs = snap_chunks / 2;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorInvalidDevice;
-    switch (choose_slices_per_wg(nheads, nslices, cus > 0 ? cus : 1)) {
-      case 4: return launch_ring32_pair<OutT, DK, 4>(a, snap_pairs, stream);
-      case 2: return launch_ring32_pair<OutT, DK, 2>(a, snap_pairs, stream);
-      default: return launch_ring32_pair<OutT, DK, 1>(a, snap_pairs, stream);
+    if constexpr (MODE != kPassOutputs) {
+      return launch_ring32_pair<OutT, DK, 1, MODE>(a, 0, stream);
+    } else {
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+      switch (choose_slices_per_wg(nheads, nslices, cus > 0 ? cus : 1)) {
+        case 4: return launch_ring32_pair<OutT, DK, 4, MODE>(a, snap_pairs, stream);
+        case 2: return launch_ring32_pair<OutT, DK, 2, MODE>(a, snap_pairs, stream);
+        default: return launch_ring32_pair<OutT, DK, 1, MODE>(a, snap_pairs, stream);
+      }
     }
   } else {
     const RecordLayout L = record_layout(DK);
     const int64_t NC = (a.T + 15) / 16;
-    hipLaunchKernelGGL((kda_state_pass<OutT, DK>), dim3(static_cast<uint32_t>(blocks)),
+    hipLaunchKernelGGL((kda_state_pass<OutT, DK, MODE>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(64), 0, stream, static_cast<const float*>(a.v),
                        static_cast<const uint8_t*>(a.workspace), a.S0, static_cast<OutT*>(a.o),
                        a.S_T, snap_chunks > 0 ? a.snapshots : nullptr, snap_chunks, a.T, a.H, a.dv,
@@ -1319,9 +1372,10 @@ hipError_t launch_prep_dk(const ChunkFwdArgs& a, hipStream_t s) {
   return a.dk == 64 ? launch_prep_gate<InT, 64>(a, s) : launch_prep_gate<InT, 128>(a, s);
 }
 
-template <typename InT, typename OutT>
+template <typename InT, typename OutT, int MODE = kPassOutputs>
 hipError_t launch_pass_dk(const ChunkFwdArgs& a, hipStream_t s) {
-  return a.dk == 64 ? launch_pass_typed<InT, OutT, 64>(a, s) : launch_pass_typed<InT, OutT, 128>(a, s);
+  return a.dk == 64 ? launch_pass_typed<InT, OutT, 64, MODE>(a, s)
+                    : launch_pass_typed<InT, OutT, 128, MODE>(a, s);
 }
 
 // T = 0: S_T is S0 (or zeros) unless it is S0 itself.
@@ -1348,6 +1402,40 @@ hipError_t launch_chunk_state_pass(const ChunkFwdArgs& a, hipStream_t stream) {
   const bool in32 = a.in_dtype == 0, out32 = a.out_dtype == 0;
   if (in32) return out32 ? launch_pass_dk<float, float>(a, stream) : launch_pass_dk<float, uint16_t>(a, stream);
   return out32 ? launch_pass_dk<uint16_t, float>(a, stream) : launch_pass_dk<uint16_t, uint16_t>(a, stream);
+}
+
+hipError_t launch_chunk_transition(const ChunkFwdArgs& a, float* F, float* E, hipStream_t stream) {
+  if (a.B * a.H == 0) return hipSuccess;
+  const bool in32 = a.in_dtype == 0;
+  if (a.T == 0) {  // F = I, E = 0
+    const int64_t n = a.B * a.H * a.dk;
+    if (F)
+      hipLaunchKernelGGL(kda_identity_states, dim3(static_cast<uint32_t>((n * a.dk + 255) / 256)),
+                         dim3(256), 0, stream, F, a.dk, n * a.dk);
+    if (E)
+      hipLaunchKernelGGL(kda_copy_state, dim3(static_cast<uint32_t>((n * a.dv + 255) / 256)),
+                         dim3(256), 0, stream, nullptr, E, n * a.dv);
+    return hipGetLastError();
+  }
+  ChunkFwdArgs t = a;
+  t.S0 = nullptr;
+  t.o = nullptr;
+  t.snapshots = nullptr;
+  t.snapshot_every = 0;
+  if (F) {  // dk columns from the identity, v = 0
+    t.dv = a.dk;
+    t.S_T = F;
+    const hipError_t e = in32 ? launch_pass_dk<float, float, kPassTransition>(t, stream)
+                              : launch_pass_dk<uint16_t, float, kPassTransition>(t, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (E) {  // the state reached from zero
+    t.dv = a.dv;
+    t.S_T = E;
+    return in32 ? launch_pass_dk<float, float, kPassState>(t, stream)
+                : launch_pass_dk<uint16_t, float, kPassState>(t, stream);
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream) {

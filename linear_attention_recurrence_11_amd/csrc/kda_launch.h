@@ -109,6 +109,17 @@ struct SpecArgs {
   int gate = kGateLogDecay;
 };
 
+// The state transition F [B, H, dk, dk] of the prepared tokens and/or the
+// state E [B, H, dk, dv] they reach from zero (either may be null), from a
+// workspace written by launch_chunk_prep; `a` supplies v, the sizes, dtype and
+// workspace.
+hipError_t launch_chunk_transition(const ChunkFwdArgs& a, float* F, float* E, hipStream_t stream);
+
+// S[r + 1] = F[r] S[r] + E[r] for r = 0 .. P-1 with S[0] = S0 (zeros when
+// null), per unit n: F [P, N, dk, dk], E [P, N, dk, dv], S [P + 1, N, dk, dv].
+hipError_t launch_affine_scan(const float* F, const float* E, const float* S0, float* S,
+                              int64_t P, int64_t N, int64_t dk, int64_t dv, hipStream_t stream);
+
 // Launch the chunkwise forward (prep kernel then state pass) on `stream`.
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream);
 // The two stages on their own (fields of `a` a stage does not use are ignored).

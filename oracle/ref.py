@@ -18,6 +18,16 @@ chunked  the same result reached chunk by chunk, written out matrix by matrix
            U = Ut - W S0,  O = Qt S0 + M U,  S_C = Diag(e^gamma) S0 + Kb^T U
          A last chunk shorter than C is just a shorter chunk.
 
+affine_scan
+         the states entering consecutive spans of a sequence from each span's
+         affine map S_out = F S_in + E (F: the span's state transition, the
+         state it reaches from the identity with v = 0; E: the state it
+         reaches from zero): S[0] = S0, S[r+1] = F[r] S[r] + E[r]. The
+         recurrence is affine in the state, which is what lets a sequence be
+         split over devices and joined afterwards (KDA context parallelism:
+         "K3 tech report" transcript, the exchange on recreating the training
+         efficiency; "Kimi K3 goes trillion-scale ..." subtitles, cue 22).
+
 Arrays are per (batch, head): q, k, g [T, dk]; v [T, dv]; beta [T]; S0 [dk, dv].
 All arithmetic is float64.
 """
@@ -83,3 +93,14 @@ def seq_batched(q, k, v, g, beta, S0=None, fn=seq, **kw):
             o[b, :, h], ST[b, h] = fn(q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h],
                                       beta[b, :, h], s0, **kw)
     return o, ST
+
+
+def affine_scan(F, E, S0=None):
+    """F [P, ..., dk, dk], E [P, ..., dk, dv], S0 [..., dk, dv] or None ->
+    S [P + 1, ..., dk, dv] with S[0] = S0 and S[r+1] = F[r] @ S[r] + E[r]."""
+    F, E = np.asarray(F, np.float64), np.asarray(E, np.float64)
+    S = np.empty((F.shape[0] + 1,) + E.shape[1:])
+    S[0] = 0.0 if S0 is None else np.asarray(S0, np.float64)
+    for r in range(F.shape[0]):
+        S[r + 1] = F[r] @ S[r] + E[r]
+    return S

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.kda_abi_version() == binding.ABI_VERSION == 2
+    assert binding.kda_abi_version() == binding.ABI_VERSION == 3
     for s in range(8):
         assert binding.kda_status_str(s) and binding.kda_status_str(s) != "unknown status"
     assert binding.kda_status_str(99) == "unknown status"
@@ -272,4 +272,44 @@ def test_spec_checks(lib):
     assert st == ALIAS
     st = lib.kda_spec_commit(*[vp(x) for x in a[1:5]], vp(a[5]), vp(a[5]), N, T, H, dk, dv, BF16, 0,
                              None)
+    assert st == ALIAS
+
+
+def test_transition_and_scan_checks(lib):
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    p, sz = fake_chunk(B=2, T=40, H=3, dk=128, dv=64, ind=BF16)
+    B, T, H, dk, dv, ind, _ = sz
+    F = BASE + (1 << 36)
+    E = F + (1 << 30)
+    tr = lambda **o: lib.kda_chunk_transition_check(
+        vp(o.get("v", p["v"])), vp(o.get("ws", p["ws"])), o.get("ws_bytes", p["ws_bytes"]),
+        vp(o.get("F", F)), vp(o.get("E", E)), B, o.get("T", T), H, o.get("dk", dk), dv, ind)
+    assert tr() == OK
+    assert tr(E=None, v=None) == OK                 # F alone reads no v
+    assert tr(v=None) == NULL                       # E needs v
+    assert tr(F=None, E=None, ws=None, ws_bytes=0) == OK
+    assert tr(ws_bytes=p["ws_bytes"] - 1) == WS
+    assert tr(E=F + 64) == ALIAS
+    assert tr(F=p["ws"]) == ALIAS
+    assert tr(E=p["v"]) == ALIAS
+    assert tr(F=F + 2) == ALIGN
+    assert tr(v=p["v"] + 8) == ALIGN
+    assert tr(dk=96) == UNSUP
+    assert tr(T=-1) == SHAPE
+    assert tr(T=0, ws=None, ws_bytes=0, v=None) == OK
+    # the workspace also holds one flag per 16 columns of the wider of dk, dv
+    assert binding.kda_chunk_fwd_workspace_size(1, 32, 64, 128, 16, BF16) == \
+        64 * 30720 + (64 * 8 * 4 + 1023) // 1024 * 1024
+    sc = lambda P=3, N=4, dk=128, dv=64, **o: lib.kda_state_affine_scan_check(
+        vp(o.get("F", F)), vp(o.get("E", E)), vp(o.get("S0", BASE)), vp(o.get("S", BASE + (1 << 38))),
+        P, N, dk, dv)
+    assert sc() == OK
+    assert sc(S0=None) == OK
+    assert sc(F=None) == NULL and sc(S=None) == NULL
+    assert sc(P=0, F=None, E=None) == OK
+    assert sc(S=F) == ALIAS and sc(S=BASE) == ALIAS
+    assert sc(F=F + 4) == ALIGN                     # F is read as 4-float vectors
+    assert sc(dk=96) == UNSUP and sc(dv=40) == UNSUP
+    assert sc(P=-1) == SHAPE
+    st = lib.kda_state_affine_scan(vp(F), vp(E), None, vp(F), 3, 4, 128, 64, None)
     assert st == ALIAS

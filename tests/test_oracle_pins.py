@@ -137,3 +137,54 @@ def test_empty_sequence_returns_initial_state():
     o, S = c_oracle.fwd(q, k, v, g, beta, S0)
     assert o.shape == (1, 0, 2, 3)
     np.testing.assert_array_equal(S, S0)
+
+
+def _span_maps(q, k, v, g, beta, bounds, form):
+    """Per span: F (the state from the identity with v = 0) and E (the state
+    from zero), both by a forward form of the oracle."""
+    dk = q.shape[1]
+    Fs, Es = [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        zero_v = np.zeros((b - a, dk), np.float32)
+        _, F = form(q[a:b], k[a:b], zero_v, g[a:b], beta[a:b], np.eye(dk))
+        _, E = form(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], None)
+        Fs.append(F)
+        Es.append(E)
+    return np.array(Fs), np.array(Es)
+
+
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_affine_scan_joins_spans(form):
+    """The recurrence is affine in the state: scanning each span's map
+    (F, E) from S0 reproduces the sequential state at every span boundary,
+    and the last one is the final state (composition of span maps)."""
+    rng = np.random.default_rng(5)
+    T, dk, dv = 70, 6, 5
+    bounds = [0, 1, 17, 40, 70]
+    q, k, v, g, beta, S0 = pins._rand(rng, T, dk, dv)
+    g[::7] = -9.0                     # beyond the floor: clamped inside every form
+    Fs, Es = _span_maps(q, k, v, g, beta, bounds, FORMS[form])
+    S = ref.affine_scan(Fs, Es, S0)
+    assert S.shape == (len(bounds), dk, dv)
+    for j, t in enumerate(bounds):
+        _, S_ref = ref.seq(q[:t], k[:t], v[:t], g[:t], beta[:t], S0)
+        assert np.abs(S[j] - S_ref).max() <= 1e-12 * max(1.0, np.abs(S_ref).max()), (form, j)
+
+
+def test_affine_scan_special_cases():
+    """Identity transitions sum the end states; zero transitions forget; an
+    empty scan returns S0; a planted transposition of F is caught."""
+    rng = np.random.default_rng(6)
+    P, dk, dv = 3, 4, 3
+    E = rng.normal(size=(P, dk, dv))
+    S0 = rng.normal(size=(dk, dv))
+    I = np.broadcast_to(np.eye(dk), (P, dk, dk))
+    S = ref.affine_scan(I, E, S0)
+    assert np.allclose(S[-1], S0 + E.sum(0), rtol=0, atol=1e-12)
+    S = ref.affine_scan(np.zeros((P, dk, dk)), E, S0)
+    assert np.allclose(S[-1], E[-1], rtol=0, atol=0)
+    assert np.array_equal(ref.affine_scan(np.zeros((0, dk, dk)), np.zeros((0, dk, dv)), S0)[0], S0)
+    F = rng.normal(size=(P, dk, dk))
+    good = ref.affine_scan(F, E, S0)
+    bad = ref.affine_scan(np.swapaxes(F, -1, -2), E, S0)
+    assert np.abs(good - bad).max() > 1e-3

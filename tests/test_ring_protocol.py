@@ -152,5 +152,5 @@ def test_launcher_instantiates_the_modelled_slice_counts():
     text = open(SRC).read()
     launch = text[text.index("switch (choose_slices_per_wg("):]
     launch = launch[:launch.index("}")]
-    found = sorted(int(x) for x in re.findall(r"launch_ring32_pair<OutT, DK, (\d+)>", launch))
+    found = sorted(int(x) for x in re.findall(r"launch_ring32_pair<OutT, DK, (\d+), MODE>", launch))
     assert found == SPWS

@@ -58,7 +58,8 @@ typedef enum {
     KDA_ERR_ALIAS = 4,        /* an output overlaps an input it must not */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required */
     KDA_ERR_HIP = 6,          /* the HIP runtime reported an error on launch */
-    KDA_ERR_ALIGNMENT = 7     /* a tensor pointer breaks its alignment rule */
+    KDA_ERR_ALIGNMENT = 7,    /* a tensor pointer breaks its alignment rule */
+    KDA_ERR_TOO_LARGE = 8     /* more scratch than kda_chunk_fwd_noalloc holds */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -352,6 +353,35 @@ kda_status kda_chunk_transition_check(const void* v, const void* workspace,
 kda_status kda_state_affine_scan_check(const float* F, const float* E, const float* S0,
                                        const float* S, int64_t P, int64_t N, int64_t dk,
                                        int64_t dv);
+
+/*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, rules and results as
+ * kda_chunk_fwd (bit for bit), minus workspace and workspace_bytes. It uses a
+ * scratch array built into the library instead: KDA_NOALLOC_SCRATCH_BYTES per
+ * device, held from the library's first use on a device until the process
+ * ends. Calls whose kda_chunk_fwd_workspace_size(...) exceeds it return
+ * KDA_ERR_TOO_LARGE before anything runs (at d = 128 with bf16 inputs that
+ * is about 2,150 pairs of chunks over all (b, h), e.g. 32 heads of 2,048
+ * tokens). It makes no allocation of its own (the first call on a device
+ * only looks up the array's device address). Every call on a device shares
+ * the one array: calls that overlap in time on the same device (on different
+ * streams, or from different threads) race and must not be issued.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const float* S0, void* o, float* S_T,
+                                 int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                 int in_dtype, int out_dtype, void* stream);
+
+/* Host-only check of kda_chunk_fwd_noalloc's arguments (see kda_chunk_fwd_check). */
+kda_status kda_chunk_fwd_noalloc_check(const void* q, const void* k, const void* v,
+                                       const void* g, const void* beta, const float* S0,
+                                       const void* o, const float* S_T, int64_t B, int64_t T,
+                                       int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                                       int out_dtype);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ _LIB = None
 
 # The argument lists below follow this version of include/kda.h.
 ABI_VERSION = 3
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_LOG_DECAY, KDA_GATE_SIGMOID = 0, 1
 _STATUS_OK = 0
@@ -84,6 +85,10 @@ def _load():
         lib.kda_state_affine_scan.argtypes = [vp] * 4 + [i64] * 4 + [vp]
         lib.kda_state_affine_scan_check.restype = i
         lib.kda_state_affine_scan_check.argtypes = [vp] * 4 + [i64] * 4
+        lib.kda_chunk_fwd_noalloc.restype = i
+        lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i64] * 5 + [i, i, vp]
+        lib.kda_chunk_fwd_noalloc_check.restype = i
+        lib.kda_chunk_fwd_noalloc_check.argtypes = [vp] * 8 + [i64] * 5 + [i, i]
         _LIB = lib
     return _LIB
 
@@ -440,3 +445,22 @@ def kda_state_affine_scan(F, E, S0=None, *, S=None, stream=None):
     if st != _STATUS_OK:
         raise KDAError(st, what)
     return S
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, S0, o, S_T=None, *, stream=None):
+    """kda_chunk_fwd using the library's built-in scratch instead of a
+    workspace (for callers that cannot allocate). The caller passes every
+    output: o [B,T,H,dv] (float32 or bfloat16) and S_T [B,H,dk,dv] float32 or
+    None. Nothing is allocated here. Returns (o, S_T)."""
+    what = "kda_chunk_fwd_noalloc"
+    lib = _load()
+    if o is None:
+        raise ValueError("%s: o is required (this call allocates nothing)" % what)
+    (B, T, H, dk, dv), specs = _fwd_specs(what, q, k, v, g, beta, S0, o, S_T, o.dtype)
+    dev = _check(what, specs)
+    st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                                   _ptr(o), _ptr(S_T), B, T, H, dk, dv, _dcode(q.dtype),
+                                   _dcode(o.dtype), _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, what)
+    return o, S_T

@@ -43,6 +43,9 @@ const char* kda_status_str(int status) {
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_HIP: return "HIP runtime error on launch";
     case KDA_ERR_ALIGNMENT: return "a tensor pointer breaks its alignment rule";
+    case KDA_ERR_TOO_LARGE:
+      return "the call needs more workspace than the built-in scratch holds "
+             "(KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
     default: return "unknown status";
   }
 }
@@ -80,6 +83,7 @@ struct ChunkPtrs {
   size_t ws_bytes;
   const float* snaps = nullptr;  // state snapshots (pass stage), or NULL
   int64_t snap_every = 0;
+  bool builtin_ws = false;       // the library's own scratch: no workspace checks
 };
 
 // The argument rules of include/kda.h for the tensors a stage touches:
@@ -103,7 +107,8 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
   if (T > 0 && prep && (!p.q || !p.k || !p.g || !p.beta)) return KDA_ERR_NULL;
   if (T > 0 && pass && (!p.v || !p.o)) return KDA_ERR_NULL;
   const size_t need = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype);
-  if (T > 0 && (!p.ws || p.ws_bytes < need)) return KDA_ERR_WORKSPACE;
+  const bool ws_checked = T > 0 && !p.builtin_ws;
+  if (ws_checked && (!p.ws || p.ws_bytes < need)) return KDA_ERR_WORKSPACE;
   const int64_t es = dsize(in_dtype), eo = dsize(out_dtype);
   if (prep) {
     const void* vec4[] = {p.q, p.k, p.g};  // read as 4-element vectors
@@ -116,7 +121,7 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
     if ((p.v && !aligned(p.v, 16)) || (p.o && !aligned(p.o, 16))) return KDA_ERR_ALIGNMENT;
     if ((p.S0 && !aligned(p.S0, 4)) || (p.S_T && !aligned(p.S_T, 4))) return KDA_ERR_ALIGNMENT;
   }
-  if (T > 0 && !aligned(p.ws, 16)) return KDA_ERR_ALIGNMENT;
+  if (ws_checked && !aligned(p.ws, 16)) return KDA_ERR_ALIGNMENT;
   const Range none{0, 0};
   const Range rq = prep ? range_of(p.q, BTH * dk, es) : none;
   const Range rk = prep ? range_of(p.k, BTH * dk, es) : none;
@@ -126,7 +131,7 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
   const Range rs0 = pass && p.S0 ? range_of(p.S0, BH * dk * dv, 4) : none;
   const Range ro = pass && T > 0 ? range_of(p.o, BTH * dv, eo) : none;
   const Range rst = pass && p.S_T ? range_of(p.S_T, BH * dk * dv, 4) : none;
-  const Range rw = T > 0 ? range_of(p.ws, static_cast<int64_t>(need), 1) : none;
+  const Range rw = ws_checked ? range_of(p.ws, static_cast<int64_t>(need), 1) : none;
   const Range ins[] = {rq, rk, rv, rg, rb, rs0};
   for (const Range& x : ins) {
     if (overlap(ro, x) || overlap(rw, x)) return KDA_ERR_ALIAS;
@@ -456,6 +461,42 @@ kda_status kda_state_affine_scan(const float* F, const float* E, const float* S0
   if (N == 0) return KDA_OK;
   return launch_status(
       kda::launch_affine_scan(F, E, S0, S, P, N, dk, dv, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+static_assert(KDA_NOALLOC_SCRATCH_BYTES == kda::kNoAllocScratchBytes,
+              "header and library disagree on the built-in scratch size");
+
+extern "C" {
+
+kda_status kda_chunk_fwd_noalloc_check(const void* q, const void* k, const void* v,
+                                       const void* g, const void* beta, const float* S0,
+                                       const void* o, const float* S_T, int64_t B, int64_t T,
+                                       int64_t H, int64_t dk, int64_t dv, int in_dtype,
+                                       int out_dtype) {
+  // the arguments as for kda_chunk_fwd; the workspace is the library's own
+  ChunkPtrs p{q, k, v, g, beta, S0, o, S_T, nullptr, 0};
+  p.builtin_ws = true;
+  const kda_status st = check_chunk(p, B, T, H, dk, dv, in_dtype, out_dtype, kPrep | kPass);
+  if (st != KDA_OK) return st;
+  if (kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype) > KDA_NOALLOC_SCRATCH_BYTES)
+    return KDA_ERR_TOO_LARGE;
+  return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, const float* S0, void* o, float* S_T,
+                                 int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                 int in_dtype, int out_dtype, void* stream) {
+  const kda_status st = kda_chunk_fwd_noalloc_check(q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv,
+                                                    in_dtype, out_dtype);
+  if (st != KDA_OK) return st;
+  if (B * H == 0) return KDA_OK;
+  void* ws = nullptr;
+  if (kda::noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
+  kda::ChunkFwdArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype, ws};
+  return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@
 // contraction slots of every dk-contraction are mapped to channels so that the
 // state slice, held in output layout, is directly the B operand of W S and
 // Qt S (no shuffles on the sequential path).
+#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1442,6 +1443,43 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream) {
   const hipError_t e = launch_chunk_prep(a, stream);
   if (e != hipSuccess) return e;
   return launch_chunk_state_pass(a, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Built-in scratch of the no-allocation forward: room for the prep records
+// and the state pass's flags of one call. Each device holds its own copy. The
+// array's name is a host-side stand-in in host code, so kernels receive the
+// device address from hipGetSymbolAddress, taken once per device with that
+// device current. Every call on a device uses the same array: calls that
+// overlap in time on one device race. Nothing in it needs clearing: the prep
+// writes every record before the pass reads it, and the plain pass writes
+// every flag before the scaled pass reads it.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace kda

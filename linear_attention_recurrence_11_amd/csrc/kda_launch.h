@@ -120,6 +120,14 @@ hipError_t launch_chunk_transition(const ChunkFwdArgs& a, float* F, float* E, hi
 hipError_t launch_affine_scan(const float* F, const float* E, const float* S0, float* S,
                               int64_t P, int64_t N, int64_t dk, int64_t dv, hipStream_t stream);
 
+// Size of the built-in device scratch of the no-allocation forward (one copy
+// per device, held until the process ends).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+// This device's address of the built-in scratch (looked up once per device,
+// with the device current); fails for devices beyond the supported count.
+hipError_t noalloc_scratch(void** ptr);
+
 // Launch the chunkwise forward (prep kernel then state pass) on `stream`.
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t stream);
 // The two stages on their own (fields of `a` a stage does not use are ignored).

@@ -11,7 +11,7 @@ from linear_attention_recurrence_11_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
-OK, NULL, SHAPE, UNSUP, ALIAS, WS, HIP, ALIGN = range(8)
+OK, NULL, SHAPE, UNSUP, ALIAS, WS, HIP, ALIGN, TOO_LARGE = range(9)
 F32, BF16 = 0, 1
 
 
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert binding.kda_abi_version() == binding.ABI_VERSION == 3
-    for s in range(8):
+    for s in range(9):
         assert binding.kda_status_str(s) and binding.kda_status_str(s) != "unknown status"
     assert binding.kda_status_str(99) == "unknown status"
 
@@ -313,3 +313,35 @@ def test_transition_and_scan_checks(lib):
     assert sc(P=-1) == SHAPE
     st = lib.kda_state_affine_scan(vp(F), vp(E), None, vp(F), 3, 4, 128, 64, None)
     assert st == ALIAS
+
+
+def test_noalloc_check(lib):
+    """The no-allocation forward applies the forward's checks and rejects
+    work beyond its built-in scratch before anything runs."""
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    limit = binding.NOALLOC_SCRATCH_BYTES
+
+    def chk(p, sz, **over):
+        p = dict(p)
+        p.update(over)
+        B, T, H, dk, dv, ind, outd = sz
+        return lib.kda_chunk_fwd_noalloc_check(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]),
+                                               vp(p["beta"]), vp(p["S0"]), vp(p["o"]),
+                                               vp(p["S_T"]), B, T, H, dk, dv, ind, outd)
+    p, sz = fake_chunk(B=1, T=2048, H=32, dk=128, dv=128, ind=BF16, ws=False)
+    assert binding.kda_chunk_fwd_workspace_size(1, 2048, 32, 128, 128, BF16) <= limit
+    assert chk(p, sz) == OK
+    assert chk(p, sz, o=p["q"]) == ALIAS
+    assert chk(p, sz, q=None) == NULL
+    p2, sz2 = fake_chunk(B=1, T=4096, H=32, dk=128, dv=128, ind=BF16, ws=False)
+    assert binding.kda_chunk_fwd_workspace_size(1, 4096, 32, 128, 128, BF16) > limit
+    assert chk(p2, sz2) == TOO_LARGE
+    assert "scratch" in binding.kda_status_str(TOO_LARGE)
+    B, T, H, dk, dv, ind, outd = sz2
+    st = lib.kda_chunk_fwd_noalloc(vp(p2["q"]), vp(p2["k"]), vp(p2["v"]), vp(p2["g"]),
+                                   vp(p2["beta"]), vp(p2["S0"]), vp(p2["o"]), vp(p2["S_T"]),
+                                   B, T, H, dk, dv, ind, outd, None)
+    assert st == TOO_LARGE                          # rejected on the host, nothing launched
+    empty = lib.kda_chunk_fwd_noalloc(None, None, None, None, None, None, None, None,
+                                      0, 5, 3, 64, 64, BF16, F32, None)
+    assert empty == OK

@@ -85,6 +85,14 @@ int kda_abi_version(void);
 const char* kda_status_str(int status);
 
 /*
+ * Failure injection, for testing callers' error handling without a failing
+ * device: the next `count` calls that pass their argument checks return
+ * KDA_ERR_HIP instead of launching, before any HIP call (count <= 0 clears
+ * it). Process-wide; meant for tests, never needed in normal use.
+ */
+void kda_debug_inject_launch_failures(int count);
+
+/*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes and input
  * dtype (0 when T, B or H is 0). Returns 0 as well for unsupported sizes;
  * kda_chunk_fwd then reports the precise error.

@@ -85,6 +85,8 @@ def _load():
         lib.kda_state_affine_scan.argtypes = [vp] * 4 + [i64] * 4 + [vp]
         lib.kda_state_affine_scan_check.restype = i
         lib.kda_state_affine_scan_check.argtypes = [vp] * 4 + [i64] * 4
+        lib.kda_debug_inject_launch_failures.restype = None
+        lib.kda_debug_inject_launch_failures.argtypes = [i]
         lib.kda_chunk_fwd_noalloc.restype = i
         lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i64] * 5 + [i, i, vp]
         lib.kda_chunk_fwd_noalloc_check.restype = i
@@ -189,6 +191,12 @@ def kda_abi_version():
 
 def kda_status_str(status):
     return _load().kda_status_str(int(status)).decode()
+
+
+def kda_debug_inject_launch_failures(count):
+    """Make the next `count` calls that pass their checks fail with KDA_ERR_HIP
+    without launching (testing error handling); 0 clears it."""
+    _load().kda_debug_inject_launch_failures(int(count))
 
 
 def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, in_dtype):

@@ -2,7 +2,9 @@
 // to the HIP launchers. See include/kda.h for the contract.
 #include "kda.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
 
 #include "kda_launch.h"
 
@@ -158,6 +160,18 @@ bool gate_ok(int gate) { return gate == KDA_GATE_LOG_DECAY || gate == KDA_GATE_S
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// Launch failures to simulate (kda_debug_inject_launch_failures): each call
+// that passed its checks and would launch takes one and returns KDA_ERR_HIP
+// instead, before any HIP call.
+std::atomic<int> g_injected_failures{0};
+
+bool injected_failure() {
+  int n = g_injected_failures.load(std::memory_order_relaxed);
+  while (n > 0)
+    if (g_injected_failures.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) return true;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +194,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
   if (st != KDA_OK) return st;
   if (B * H == 0) return KDA_OK;
   kda::ChunkFwdArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype, workspace};
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -210,6 +225,7 @@ kda_status kda_chunk_fwd_ex(const void* q, const void* k, const void* v, const v
   a.gate = gate;
   a.snapshots = snapshots;
   a.snapshot_every = snapshot_every;
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -222,6 +238,7 @@ kda_status kda_chunk_prep(const void* q, const void* k, const void* g, const voi
   if (B * H == 0 || T == 0) return KDA_OK;
   kda::ChunkFwdArgs a{q, k, nullptr, g, beta, nullptr, nullptr, nullptr, B, T, H, dk, dv,
                       in_dtype, KDA_F32, workspace};
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_chunk_prep(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -235,6 +252,7 @@ kda_status kda_chunk_state_pass(const void* v, const void* workspace, size_t wor
   if (B * H == 0) return KDA_OK;
   kda::ChunkFwdArgs a{nullptr, nullptr, v, nullptr, nullptr, S0, o, S_T, B, T, H, dk, dv,
                       in_dtype, out_dtype, const_cast<void*>(workspace)};
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_chunk_state_pass(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -284,6 +302,7 @@ kda_status kda_decode_step_ex(const void* q, const void* k, const void* v, const
   if (N * H == 0) return KDA_OK;
   kda::DecodeArgs a{q, k, v, g, beta, S, o, N, H, dk, dv, in_dtype, out_dtype};
   a.gate = gate;
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_decode_step(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -347,6 +366,7 @@ kda_status kda_spec_verify(const void* q, const void* k, const void* v, const vo
   kda::SpecArgs a{q, k, v, g, beta, const_cast<float*>(S), o, nullptr, N, T, H, dk, dv,
                   in_dtype, out_dtype};
   a.gate = gate;
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_spec(a, false, static_cast<hipStream_t>(stream)));
 }
 
@@ -366,6 +386,7 @@ kda_status kda_spec_commit(const void* k, const void* v, const void* g, const vo
   if (N * H == 0 || T == 0) return KDA_OK;
   kda::SpecArgs a{nullptr, k, v, g, beta, S, nullptr, accepted, N, T, H, dk, dv, in_dtype, KDA_F32};
   a.gate = gate;
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_spec(a, true, static_cast<hipStream_t>(stream)));
 }
 
@@ -445,6 +466,7 @@ kda_status kda_chunk_transition(const void* v, const void* workspace, size_t wor
   if (B * H == 0 || (!F && !E)) return KDA_OK;
   kda::ChunkFwdArgs a{nullptr, nullptr, v, nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H,
                       dk, dv, in_dtype, KDA_F32, const_cast<void*>(workspace)};
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(kda::launch_chunk_transition(a, F, E, static_cast<hipStream_t>(stream)));
 }
 
@@ -459,6 +481,7 @@ kda_status kda_state_affine_scan(const float* F, const float* E, const float* S0
   const kda_status st = check_scan(F, E, S0, S, P, N, dk, dv);
   if (st != KDA_OK) return st;
   if (N == 0) return KDA_OK;
+  if (injected_failure()) return KDA_ERR_HIP;
   return launch_status(
       kda::launch_affine_scan(F, E, S0, S, P, N, dk, dv, static_cast<hipStream_t>(stream)));
 }
@@ -493,10 +516,19 @@ kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, co
                                                     in_dtype, out_dtype);
   if (st != KDA_OK) return st;
   if (B * H == 0) return KDA_OK;
+  if (injected_failure()) return KDA_ERR_HIP;
   void* ws = nullptr;
   if (kda::noalloc_scratch(&ws) != hipSuccess) return KDA_ERR_HIP;
   kda::ChunkFwdArgs a{q, k, v, g, beta, S0, o, S_T, B, T, H, dk, dv, in_dtype, out_dtype, ws};
   return launch_status(kda::launch_chunk_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+void kda_debug_inject_launch_failures(int count) {
+  g_injected_failures.store(count > 0 ? count : 0, std::memory_order_relaxed);
 }
 
 }  // extern "C"

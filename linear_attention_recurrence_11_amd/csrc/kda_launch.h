@@ -2,7 +2,7 @@
 // kernel translation units. Not part of the public ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 

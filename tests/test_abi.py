@@ -345,3 +345,38 @@ def test_noalloc_check(lib):
     empty = lib.kda_chunk_fwd_noalloc(None, None, None, None, None, None, None, None,
                                       0, 5, 3, 64, 64, BF16, F32, None)
     assert empty == OK
+
+
+def test_injected_launch_failures(lib):
+    """A call that passes its checks takes an injected failure and returns
+    KDA_ERR_HIP without any HIP call (every call here uses fake pointers and
+    must not launch); a call that fails its checks reports that first and
+    leaves the count alone."""
+    vp = ctypes.c_void_p
+    a = [BASE + i * (1 << 24) for i in range(7)]   # q k v g beta S o
+    dec = lambda o=a[6]: lib.kda_decode_step(*[vp(x) for x in a[:6]], vp(o), 4, 2, 128, 128, BF16,
+                                             F32, None)
+    try:
+        binding.kda_debug_inject_launch_failures(2)
+        assert dec() == HIP
+        assert dec(o=a[5]) == ALIAS                 # checks first; count untouched
+        assert dec() == HIP                         # the second injected failure
+        binding.kda_debug_inject_launch_failures(1)
+        p, sz = fake_chunk()
+        B, T, H, dk, dv, ind, outd = sz
+        st = lib.kda_chunk_fwd(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]), vp(p["beta"]),
+                               vp(p["S0"]), vp(p["o"]), vp(p["S_T"]), B, T, H, dk, dv, ind, outd,
+                               vp(p["ws"]), p["ws_bytes"], None)
+        assert st == HIP
+        binding.kda_debug_inject_launch_failures(1)
+        F = BASE + (1 << 36)
+        st = lib.kda_state_affine_scan(vp(F), vp(F + (1 << 30)), None, vp(F + (1 << 31)), 2, 3,
+                                       128, 64, None)
+        assert st == HIP
+        binding.kda_debug_inject_launch_failures(1)
+        st = lib.kda_chunk_fwd_noalloc(vp(p["q"]), vp(p["k"]), vp(p["v"]), vp(p["g"]),
+                                       vp(p["beta"]), vp(p["S0"]), vp(p["o"]), vp(p["S_T"]),
+                                       B, T, H, dk, dv, ind, outd, None)
+        assert st == HIP                            # taken before the scratch lookup
+    finally:
+        binding.kda_debug_inject_launch_failures(0)

@@ -10,6 +10,12 @@ One step = the whole hot path over one batch of synthetic input:
 Inputs are generated on the GPU before timing (seeded, synthetic). Every
 kernel launch is bracketed by HIP events on the stream it runs on.
 
+After the timed steps: the options built on the path (bf16 output,
+snapshots, speculative verify/commit, the span-by-span prefill through the
+context-split entry points), the other forward workloads, and the fp64 C
+oracle (test infrastructure) on the host's cores beside every workload,
+whose outputs also check the GPU's element by element.
+
 Prints one JSON line. `value` is prefill tokens/s (B*T / prefill time).
 """
 import argparse
@@ -27,13 +33,19 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PREFILL_MFMA_TARGET = 0.40      # stated target for the prefill, as a fraction of bf16 peak
+DECODE_HBM_TARGET = 0.70        # stated target for the decode step, as a fraction of HBM peak
 
 
-def prefill_units(B, T, H, dk, dv, C=16):
-    """Algorithmic work per token-head of the prefill path (bf16 in, fp32 o):
-    flops 6 dk dv + 4C dk + 2C dv + C(dk+dv); bytes q,k,g,v (bf16) + beta + o."""
+def log(*parts):
+    print("[bench]", *parts, file=sys.stderr, flush=True)
+
+
+def prefill_units(dk, dv, in_bytes=2, C=16):
+    """Algorithmic work per token-head of the prefill path (fp32 o):
+    flops 6 dk dv + 4C dk + 2C dv + C(dk+dv); bytes q,k,g,v + beta in, o out."""
     flops = 6 * dk * dv + 4 * C * dk + 2 * C * dv + C * (dk + dv)
-    bytes_ = 2 * (3 * dk + dv) + 2 + 4 * dv
+    bytes_ = in_bytes * (3 * dk + dv + 1) + 4 * dv
     return flops, bytes_
 
 
@@ -64,11 +76,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg")
-    ap.add_argument("--cpu-tokens", type=int, default=32768,
-                    help="tokens (all 32 heads) of the prefill workload the oracle runs")
+    ap.add_argument("--cpu-1m-tokens", type=int, default=16384,
+                    help="leading tokens (all heads) of the 1M-token workload the oracle runs")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the snapshot / speculative-decoding measurements and the other "
-                         "forward workloads (profiling runs)")
+                    help="skip the option measurements and the other forward workloads "
+                         "(profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -88,16 +100,23 @@ def main():
     pf = configs.PREFILL_64K
     dc = configs.DECODE
     B, T, H, dk, dv = pf.B, pf.T, pf.H, pf.dk, pf.dv
-    print("[bench] generating %s and %s" % (pf.name, dc.name), file=sys.stderr, flush=True)
+    log("generating %s and %s" % (pf.name, dc.name))
     ins = inputs.make_workload(pf, device=dev)
     code = 1  # bf16 inputs
-    ws_bytes = binding.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(binding.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code),
+                     dtype=torch.uint8, device=dev)
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
     ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     d = inputs.make_workload(dc, device=dev)
-    S = d["S"]
     N, steps = dc.B, dc.T
+    # one untimed 64-step run from the workload's initial states, kept for the
+    # oracle's check; the timed steps then advance a copy in place
+    S0_dec = d["S"].clone()
+    S = d["S"].clone()
+    dec_check = [binding.kda_decode_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S)
+                 for s in range(steps)]
+    dec_check = (torch.stack(dec_check).cpu(), S.cpu())
+    S.copy_(S0_dec)
     o_dec = torch.empty((N, dc.H, dc.dv), dtype=torch.float32, device=dev)
     copy_src = copy_dst = None
     if args.copy_calibration:
@@ -123,12 +142,12 @@ def main():
 
     nev = 3 + 2 * steps
     new_events = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step(new_events())
     torch.cuda.synchronize()
 
-    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    log("timing %d steps" % args.steps)
     all_ev = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -142,17 +161,20 @@ def main():
     pass_ms = np.array([e[1].elapsed_time(e[2]) for e in all_ev])
     dec_ms = np.array([[e[3 + 2 * s].elapsed_time(e[4 + 2 * s]) for s in range(steps)] for e in all_ev])
     prefill_ms = prep_ms + pass_ms
+    # host copies for the oracle's check of this workload (o of the last step)
+    pf_check = (o.cpu(), ST.cpu())
 
     nxt = None
     if not args.no_next:
-        nxt = measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, dev, np, torch)
+        nxt = measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, dev, np,
+                           torch)
     tokens = B * T
     value = tokens / (prefill_ms.mean() * 1e-3)
 
     # ---- rooflines (algorithmic work / measured average launch time) ----
     th = B * T * H
-    f_tok, b_tok = prefill_units(B, T, H, dk, dv)
-    state_bytes = 2 * dk * dv * 4                         # S_T write + S0 read
+    f_tok, b_tok = prefill_units(dk, dv)
+    state_bytes = 2 * dk * dv * 4                         # state read + write
     prep_bytes = th * (2 * 3 * dk + 2)                    # q, k, g, beta in
     pass_bytes = th * (2 * dv + 4 * dv) + B * H * dk * dv * 4  # v in, o out, S_T out (S0 = 0)
     path_bytes = th * b_tok + B * H * dk * dv * 4
@@ -160,23 +182,38 @@ def main():
     dec_bytes = N * dc.H * dec_unit_bytes
     dec_state_bytes = N * dc.H * state_bytes
 
-    def roof(name, nbytes, ms, sources, bound="hbm"):
+    def roof(name, nbytes, ms, bound="hbm"):
         achieved = nbytes / (ms * 1e-3) / 1e9
-        traffic = load_traffic(name)
         return {"kernel": name, "bound": bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": int(nbytes),
+                "traffic": load_traffic(name), "algorithmic_bytes_per_launch": int(nbytes),
                 "avg_launch_us": round(ms * 1e3, 2)}
 
-    r_dec = roof("kda_decode_kernel", dec_bytes, dec_ms.mean(), ["linear_attention_recurrence_11_amd/csrc/kda_decode.hip"])
-    r_prep = roof("kda_chunk_prep", prep_bytes, prep_ms.mean(), ["linear_attention_recurrence_11_amd/csrc/kda_chunk.hip"])
-    r_pass = roof("kda_state_pass", pass_bytes, pass_ms.mean(), ["linear_attention_recurrence_11_amd/csrc/kda_chunk.hip"])
+    r_dec = roof("kda_decode_kernel", dec_bytes, dec_ms.mean())
+    r_dec["target_frac"] = DECODE_HBM_TARGET
+    r_prep = roof("kda_chunk_prep", prep_bytes, prep_ms.mean())
+    r_pass = roof("kda_state_pass", pass_bytes, pass_ms.mean())
     step_share = {"kda_decode_kernel": dec_ms.sum(1).mean(), "kda_chunk_prep": prep_ms.mean(),
                   "kda_state_pass": pass_ms.mean()}
     dominant = max(step_share, key=step_share.get)
     roofs = {"kda_decode_kernel": r_dec, "kda_chunk_prep": r_prep, "kda_state_pass": r_pass}
     prefill_gbps = path_bytes / (prefill_ms.mean() * 1e-3) / 1e9
     prefill_tflops = th * f_tok / (prefill_ms.mean() * 1e-3) / 1e12
+    # the prefill path's own roofline, beside the headline value it belongs to:
+    # HBM-bound at this shape (74.6 flop/B < the ~315 flop/B ridge), reported
+    # against both peaks; the matrix-core fraction counts algorithmic flops only
+    roof_prefill = {
+        "path": "kda_chunk_prep + kda_chunk_state_pass", "bound": "hbm",
+        "achieved": round(prefill_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(prefill_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": (None if load_traffic("kda_chunk_prep") is None or load_traffic("kda_state_pass") is None
+                    else load_traffic("kda_chunk_prep") + load_traffic("kda_state_pass")),
+        "algorithmic_bytes_per_launch": int(path_bytes), "avg_ms": round(prefill_ms.mean(), 4),
+        "mfma_achieved_TFLOPs": round(prefill_tflops, 2), "mfma_peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+        "mfma_frac": round(prefill_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "mfma_target_frac": PREFILL_MFMA_TARGET,
+        "mfma_frac_at_hbm_roof": round(f_tok / b_tok / (BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)), 4),
+    }
 
     rec = {
         "metric": METRIC,
@@ -195,6 +232,8 @@ def main():
                    "in_dtype": "bf16", "state_dtype": "f32", "out_dtype": "f32",
                    "decode_workload": dc.name, "decode_requests": N, "decode_steps": steps},
         "roofline": roofs[dominant],
+        "roofline_prefill": roof_prefill,
+        "roofline_decode": r_dec,
         "prefill": {
             "tokens_per_s": round(value, 1), "ms": round(prefill_ms.mean(), 4),
             "median_ms": round(float(np.median(prefill_ms)), 4),
@@ -213,13 +252,18 @@ def main():
             "steps_per_launch_set": steps,
         },
         "kernels": roofs,
+        "dominant_kernel_by_step_time": dominant,
         "next": nxt,
     }
+    checks = {"prefill_64k": pf_check, "decode": dec_check}
+    del ws
+    torch.cuda.empty_cache()
     if not args.no_next:
-        # the other forward workloads, one after another, after the 64K inputs are released
-        del ws
-        torch.cuda.empty_cache()
-        rec["other_workloads"] = measure_workloads(binding, configs, inputs, stream, dev, np, torch)
+        # the other forward workloads, one after another, after the 64K workspace is released
+        rec["other_workloads"], other_checks = measure_workloads(binding, configs, inputs, stream,
+                                                                 dev, np, torch,
+                                                                 args.cpu_1m_tokens)
+        checks.update(other_checks)
 
     # practical HBM ceiling for context: a plain device-to-device copy
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -238,17 +282,23 @@ def main():
     del src, dst
 
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"], rec["sampled_parity"] = cpu_leg(ins, o, args.cpu_tokens, pf)
+        per, parity = cpu_leg(configs, inputs, dev, torch, np, checks, args.cpu_1m_tokens,
+                              rec.get("other_workloads"), value, rec["decode"]["us_per_step"])
+        top = dict(per[0])
+        top["per_config"] = per
+        rec["cpu_baseline"] = top
+        rec["parity"] = parity
     print(json.dumps(rec), flush=True)
 
 
 def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, dev, np, torch,
-                 reps=5, every=512, draft=4, accept=2):
+                 reps=5, every=512, draft=4, accept=2, spans=4):
     """The options built on the path, timed after the steps with HIP events:
     the prefill with bf16 output, the prefill with a state snapshot every
-    `every` tokens (prefix reuse), and
-    speculative verify of `draft` tokens + commit of `accept` of them for the
-    decode batch, against the decode steps they replace."""
+    `every` tokens (prefix reuse), speculative verify of `draft` tokens +
+    commit of `accept` of them for the decode batch against the decode steps
+    they replace, and the prefill computed span by span through the
+    context-split entry points (one GPU)."""
     ev = lambda: torch.cuda.Event(enable_timing=True)
     snaps = torch.empty((B, T // every, H, dk, dv), dtype=torch.float32, device=dev)
 
@@ -274,6 +324,9 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     bf16_ms = timed(lambda: binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
                                                   ins["S0"], o=o16, S_T=ST, workspace=ws))
     del o16
+    # the state transition of the whole sequence (dk columns, no v, no outputs)
+    trans_ms = timed(lambda: binding.kda_chunk_transition(ws, B, T, H, dk, dv, torch.bfloat16))
+    ctx = measure_context_split(binding, ins, B, T, H, dk, dv, spans, stream, dev, np, torch)
     N, Hd, dkd, dvd = d["S"].shape
     sp = inputs.make_forward(N, draft, Hd, dkd, dvd, "bf16", s0="zero", seed=4321, device=dev)
     Sck = d["S"].clone()
@@ -299,6 +352,9 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
                       "bytes": B * (T // every) * H * dk * dv * 4,
                       "prefill_ms": round(snap_ms, 4), "plain_prefill_ms": round(plain_ms, 4),
                       "overhead_frac": round(snap_ms / plain_ms - 1.0, 4)},
+        "transition": {"what": "kda_chunk_transition, F only, over the prepared 64K-token workload",
+                       "ms": round(trans_ms, 4)},
+        "context_split": ctx,
         "spec": {"requests": N, "heads": Hd, "draft_tokens": draft, "accepted": accept,
                  "verify_us": round(ver_ms * 1e3, 2),
                  "verify_GBps": round(ver_bytes / (ver_ms * 1e-3) / 1e9, 1),
@@ -309,12 +365,70 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     }
 
 
-def measure_workloads(binding, configs, inputs, stream, dev, np, torch):
+def measure_context_split(binding, ins, B, T, H, dk, dv, spans, stream, dev, np, torch, reps=3):
+    """The 64K prefill cut into `spans` equal spans and computed span by span
+    on this GPU through the context-split entry points: per span kda_chunk_prep
+    and kda_chunk_transition (F and E; the last span needs neither), one
+    kda_state_affine_scan, then kda_chunk_state_pass per span from its entering
+    state. Phase times are HIP-event measured; the result is checked against
+    the plain forward."""
+    L = T // spans
+    xs = [{n: ins[n][:, r * L:(r + 1) * L].contiguous() for n in ("q", "k", "v", "g", "beta")}
+          for r in range(spans)]
+    wss = [torch.empty(binding.kda_chunk_fwd_workspace_size(B, L, H, dk, dv, 1), dtype=torch.uint8,
+                       device=dev) for _ in range(spans)]
+    Fs = torch.empty((spans - 1, B * H, dk, dk), dtype=torch.float32, device=dev)
+    Es = torch.empty((spans - 1, B * H, dk, dv), dtype=torch.float32, device=dev)
+    Sin = torch.empty((spans, B * H, dk, dv), dtype=torch.float32, device=dev)
+    os_ = [torch.empty((B, L, H, dv), dtype=torch.float32, device=dev) for _ in range(spans)]
+    ST = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    S0 = torch.zeros((B * H, dk, dv), dtype=torch.float32, device=dev)
+    times = []
+    for r in range(reps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        e[0].record(stream)
+        for x, w in zip(xs, wss):
+            binding.kda_chunk_prep(x["q"], x["k"], x["g"], x["beta"], dv, workspace=w)
+        e[1].record(stream)
+        for j in range(spans - 1):
+            binding.kda_chunk_transition(wss[j], B, L, H, dk, dv, torch.bfloat16, v=xs[j]["v"],
+                                         F=Fs[j].view(B, H, dk, dk), E=Es[j].view(B, H, dk, dv))
+        e[2].record(stream)
+        binding.kda_state_affine_scan(Fs, Es, S0, S=Sin)
+        e[3].record(stream)
+        for j in range(spans):
+            binding.kda_chunk_state_pass(xs[j]["v"], wss[j], dk, Sin[j].view(B, H, dk, dv), o=os_[j],
+                                         S_T=ST if j == spans - 1 else None,
+                                         want_state=j == spans - 1)
+        e[4].record(stream)
+        torch.cuda.synchronize()
+        if r:
+            times.append([e[i].elapsed_time(e[i + 1]) for i in range(4)])
+    t = np.mean(times, axis=0)
+    o_ref, S_ref = binding.kda_chunk_fwd(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"],
+                                         ins["S0"])
+    o = torch.cat(os_, 1)
+    torch.cuda.synchronize()
+    rms = float(o_ref.double().pow(2).mean().sqrt())
+    diff = float((o - o_ref).abs().max()) / rms
+    diff_s = float((ST - S_ref).abs().max()) / float(S_ref.double().pow(2).mean().sqrt())
+    del xs, wss, Fs, Es, Sin, os_, o, o_ref
+    return {"spans": spans, "tokens_per_span": L, "prep_ms": round(float(t[0]), 4),
+            "transition_ms": round(float(t[1]), 4), "scan_ms": round(float(t[2]), 4),
+            "state_pass_ms": round(float(t[3]), 4), "total_ms": round(float(t.sum()), 4),
+            "o_max_abs_diff_vs_plain_forward_over_rms": diff,
+            "S_T_max_abs_diff_vs_plain_forward_over_rms": diff_s}
+
+
+def measure_workloads(binding, configs, inputs, stream, dev, np, torch, cpu_1m_tokens):
     """kda_chunk_fwd (prep + state pass) on the forward workloads other than
-    the 64K prefill, each timed with HIP events around its two launches."""
-    out = []
-    for w in (configs.SMALL_FWD, configs.MID_FWD, configs.PREFILL_1M):
-        print("[bench] workload %s" % w.name, file=sys.stderr, flush=True)
+    the 64K prefill, each timed with HIP events around its two launches.
+    Returns the timings and host copies of the outputs for the oracle's
+    check (the 1M-token workload: o over its leading tokens)."""
+    out, checks = [], {}
+    for key, w in (("fwd_small", configs.SMALL_FWD), ("fwd_mid", configs.MID_FWD),
+                   ("prefill_1m", configs.PREFILL_1M)):
+        log("workload %s" % w.name)
         ins = inputs.make_workload(w, device=dev)
         code = 0 if w.in_dtype == "f32" else 1
         ws = torch.empty(binding.kda_chunk_fwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv, code),
@@ -337,7 +451,7 @@ def measure_workloads(binding, configs, inputs, stream, dev, np, torch):
         ms = float(np.mean(np.add(prep, pas)))
         th = w.B * w.T * w.H
         es = 4 if code == 0 else 2
-        flops = 6 * w.dk * w.dv + 4 * 16 * w.dk + 2 * 16 * w.dv + 16 * (w.dk + w.dv)
+        flops, _ = prefill_units(w.dk, w.dv, es)
         nbytes = th * (es * (3 * w.dk + w.dv + 1) + 4 * w.dv) + w.B * w.H * w.dk * w.dv * 4 * \
             (2 if ins["S0"] is not None else 1)
         gbps = nbytes / (ms * 1e-3) / 1e9
@@ -352,45 +466,110 @@ def measure_workloads(binding, configs, inputs, stream, dev, np, torch):
                     "algorithmic_GBps": round(gbps, 1), "frac_of_hbm_roof": round(gbps / HBM_PEAK_GBPS, 4),
                     "algorithmic_TFLOPs": round(tflops, 3),
                     "frac_of_matrix_peak": round(tflops / peak, 5), "matrix_peak_TFLOPs": peak})
+        if w.T > 65536:
+            checks[key] = (o[:, :cpu_1m_tokens].cpu(), None)
+        else:
+            checks[key] = (o.cpu(), ST.cpu())
         del ins, ws, o, ST
         torch.cuda.empty_cache()
-    return out
+    return out, checks
 
 
-def cpu_leg(ins, o, ntok, pf):
-    """The fp64 oracle (test infrastructure) on the first `ntok` tokens of all
-    heads of the prefill workload, timed on this host's cores; its outputs also
-    check the GPU outputs for those tokens."""
-    import numpy as np
-
-    from linear_attention_recurrence_11_amd import inputs
+def cpu_leg(configs, inputs, dev, torch, np, checks, cpu_1m_tokens, other, gpu_value,
+            dec_us):
+    """The fp64 C oracle (test infrastructure) beside every workload, timed on
+    this host's cores with the same seeded inputs; its outputs check the GPU
+    outputs kept from the runs above. Returns (per-config baselines, parity)."""
     from oracle import c_oracle
 
-    ntok = min(ntok, pf.T)
     to = inputs.to_oracle
-    host = {n: to(ins[n][:, :ntok].contiguous()) for n in ("q", "k", "v", "g", "beta")}
     threads = c_oracle.default_threads()
-    print("[bench] oracle on %d tokens x %d heads, %d threads" % (ntok, pf.H, threads),
-          file=sys.stderr, flush=True)
+    per, parity = [], {}
+    gpu_rates = {w["workload"]: w["tokens_per_s"] for w in (other or [])}
+
+    def err(x, ref):
+        x = np.asarray(x, np.float64)
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        return float(np.abs(x - ref).max() / rms) if rms > 0 else float(np.abs(x - ref).max())
+
+    def forward_case(key, w, ntok, sample):
+        ins = inputs.make_workload(w, device=dev)
+        host = {n: to(ins[n][:, :ntok].contiguous()) for n in ("q", "k", "v", "g", "beta")}
+        S0 = None if ins["S0"] is None else ins["S0"].cpu().numpy()
+        del ins
+        torch.cuda.empty_cache()
+        log("oracle: %s, %d tokens x %d heads x %d, %d threads" % (w.name, ntok, w.H, w.B, threads))
+        t0 = time.perf_counter()
+        o_ref, S_ref = c_oracle.fwd(host["q"], host["k"], host["v"], host["g"], host["beta"], S0,
+                                    nthreads=threads)
+        wall = time.perf_counter() - t0
+        # per-core rate: one (b, h) on one thread, over at most 8192 tokens
+        n1 = min(ntok, 8192)
+        one = {n: np.ascontiguousarray(x[:1, :n1, :1]) for n, x in host.items()}
+        t0 = time.perf_counter()
+        c_oracle.fwd(one["q"], one["k"], one["v"], one["g"], one["beta"],
+                     None if S0 is None else S0[:1, :1], nthreads=1)
+        wall1 = time.perf_counter() - t0
+        o_gpu, S_gpu = checks.get(key, (None, None))
+        if o_gpu is not None:
+            p = {"err_o_max_over_rms": err(o_gpu[:, :ntok].numpy(), o_ref), "tokens": ntok,
+                 "tolerance": 1e-4 if w.in_dtype == "f32" else 2e-2}
+            if S_gpu is not None and ntok == w.T:
+                p["err_S_T_max_over_rms"] = err(S_gpu.numpy(), S_ref)
+            parity[w.name] = p
+        rate = w.B * ntok / wall
+        gpu = gpu_value if key == "prefill_64k" else gpu_rates.get(w.name)
+        return {"workload": w.name, "value": round(rate, 1), "unit": "tokens/s", "cores": threads,
+                "kind": "oracle", "wall_s": round(wall, 3), "sample": sample,
+                "gpu_tokens_per_s": gpu,
+                "one_core": {"token_heads_per_s": round(n1 / wall1, 1), "wall_s": round(wall1, 3),
+                             "sample": "%d tokens of one (b, h), one thread" % n1}}
+
+    pf = configs.PREFILL_64K
+    per.append(forward_case("prefill_64k", pf, pf.T, "fp64 C oracle, all %d tokens of all %d heads "
+                            "of %s (o and S_T compared element-wise)" % (pf.T, pf.H, pf.name)))
+    if other is not None:
+        for key, w in (("fwd_small", configs.SMALL_FWD), ("fwd_mid", configs.MID_FWD)):
+            per.append(forward_case(key, w, w.T, "fp64 C oracle, the whole workload %s" % w.name))
+        w = configs.PREFILL_1M
+        n = min(cpu_1m_tokens, w.T)
+        per.append(forward_case("prefill_1m", w, n, "fp64 C oracle, the first %d of %d tokens of all "
+                                "%d heads of %s (o compared on those tokens)" % (n, w.T, w.H, w.name)))
+    # decode: 64 single-token steps over all (request, head) units
+    dc = configs.DECODE
+    d = inputs.make_workload(dc, device=dev)
+    host = {n: to(d[n]) for n in ("q", "k", "v", "g", "beta")}
+    S = d["S"].cpu().numpy().astype(np.float64)
+    del d
+    torch.cuda.empty_cache()
+    log("oracle: %s, %d threads" % (dc.name, threads))
     t0 = time.perf_counter()
-    o_ref, _ = c_oracle.fwd(host["q"], host["k"], host["v"], host["g"], host["beta"], None,
-                            nthreads=threads, want_state=False)
+    outs = []
+    for s in range(dc.T):
+        o_s, S = c_oracle.fwd(host["q"][s][:, None], host["k"][s][:, None], host["v"][s][:, None],
+                              host["g"][s][:, None], host["beta"][s][:, None], S, nthreads=threads)
+        outs.append(o_s[:, 0])
     wall = time.perf_counter() - t0
-    og = o[:, :ntok].float().cpu().numpy()
-    err = float(np.abs(og - o_ref).max() / np.sqrt(np.mean(o_ref ** 2)))
-    # per-core rate: the same tokens of one head on one thread
-    one = {n: np.ascontiguousarray(x[:, :, :1]) for n, x in host.items()}
+    o_gpu, S_gpu = checks["decode"]
+    parity[dc.name] = {"err_o_max_over_rms": err(o_gpu.numpy(), np.stack(outs)),
+                       "err_S_max_over_rms": err(S_gpu.numpy(), S), "steps": dc.T, "tolerance": 2e-2}
+    units = dc.B * dc.H
     t0 = time.perf_counter()
-    c_oracle.fwd(one["q"], one["k"], one["v"], one["g"], one["beta"], None, nthreads=1,
-                 want_state=False)
+    S1 = np.zeros((1, dc.H, dc.dk, dc.dv))
+    for s in range(dc.T):
+        _, S1 = c_oracle.fwd(host["q"][s][:1, None], host["k"][s][:1, None], host["v"][s][:1, None],
+                             host["g"][s][:1, None], host["beta"][s][:1, None], S1, nthreads=1)
     wall1 = time.perf_counter() - t0
-    base = {"value": round(pf.B * ntok / wall, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "wall_s": round(wall, 2),
-            "sample": "fp64 C oracle, first %d of %d tokens, all %d heads of %s" % (ntok, pf.T, pf.H, pf.name),
-            "one_core": {"token_heads_per_s": round(pf.B * ntok / wall1, 1), "wall_s": round(wall1, 2),
-                         "sample": "the same tokens of head 0, one thread"}}
-    parity = {"err_o_max_over_rms": err, "tokens": ntok, "heads": pf.H, "tolerance": 2e-2}
-    return base, parity
+    per.append({"workload": dc.name, "value": round(units * dc.T / wall, 1),
+                "unit": "request-head steps/s", "cores": threads, "kind": "oracle",
+                "wall_s": round(wall, 3),
+                "sample": "fp64 C oracle, all %d steps of all %d requests x %d heads (o of every step "
+                          "and the final states compared element-wise)" % (dc.T, dc.B, dc.H),
+                "gpu_request_head_steps_per_s": round(units / (dec_us * 1e-6), 1),
+                "one_core": {"request_head_steps_per_s": round(dc.H * dc.T / wall1, 1),
+                             "wall_s": round(wall1, 3),
+                             "sample": "%d steps of one request (%d heads), one thread" % (dc.T, dc.H)}})
+    return per, parity
 
 
 if __name__ == "__main__":

@@ -1217,13 +1217,20 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   for (int64_t k = NPR; k < NPS; ++k) ring_barrier();  // match the loader's steps
   if constexpr (!SCALED) {
     // suspect: a non-finite entry anywhere in the slice (the sum keeps it),
-    // or every entry below kScaleLow
+    // or every entry below kScaleLow while some are still normal fp32 values.
+    // Once fp16 operands underflow, the plain pass keeps only the decay of the
+    // fp32 state (an upper bound on its size, since the rest of each step is
+    // a contraction for keys of norm at most 1), so a state that ends below
+    // the smallest normal fp32 value is below fp32's range however it is
+    // computed (e.g. the transition of a long span), and is not redone.
     float sum = 0.f;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sum += fabsf(S[m][i]);
-    const bool suspect = __any(!(sum <= 3.4028235e38f)) || !__any(state_max(S) >= kScaleLow);
+    const float ms = state_max(S);
+    const bool suspect = __any(!(sum <= 3.4028235e38f)) ||
+                         (!__any(ms >= kScaleLow) && __any(ms >= 1.17549435e-38f));
     if (l == 0) flags[head * (DV / 16) + slice] = suspect ? 1 : 0;
     if (suspect) return;
   }

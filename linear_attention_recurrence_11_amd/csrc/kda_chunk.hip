@@ -17,8 +17,9 @@
 // trillion-scale with sparse MoE efficiency" subtitles, cue 14).
 //
 // Two phases, each a kernel:
-//  prep         all chunks in parallel: decay scan with DPP row scans (a
-//               16-lane row = the 16 tokens of a chunk), scaled operands, Gram
+//  prep         all chunks in parallel: decay scan with a DPP row scan (a
+//               16-lane row = the 16 tokens of a chunk) and a row broadcast of
+//               its last token for e^gamma, scaled operands, Gram
 //               tiles A and M on the matrix cores, (I + A)^-1 by forward
 //               substitution in LDS, W on the matrix cores; writes workspace
 //               records in matrix-core fragment order.
@@ -156,20 +157,19 @@ __global__ __launch_bounds__(64) void kda_chunk_prep(const float* __restrict__ q
         // padded tokens past T carry log-decay 0 whatever the gate
         const float x = (valid ? gate_decay<GATE>(xg[i]) : 0.f) * kLog2e;
         const float G = row_inclusive_prefix_sum(x);    // log2 e^Gamma_r
-        const float Gb = row_exclusive_suffix_sum(x);   // log2 e^(gamma - Gamma_r)
-        // the -5 floor bounds |G|, |Gb| by 80 log2(e) over 16 tokens, so every
-        // power of two here is a normal float: the hardware exp2 needs no
-        // range reduction
+        // the -5 floor bounds |G| by 80 log2(e) over 16 tokens, so every power
+        // of two here is a normal float: the hardware exp2 needs no range
+        // reduction
         const float E = __builtin_amdgcn_exp2f(G);
         const float Eh = __builtin_amdgcn_exp2f(-G);
-        const float Eb = __builtin_amdgcn_exp2f(Gb);
+        const float Eg = row_broadcast_last(E);  // e^gamma, the decay to the chunk's end
         const int j = 4 * jj + i;
         qt[j] = E * xq[i];
         kt[j] = E * xk[i];
         kh[j] = Eh * xk[i];
         eg[j] = E;
         s_kt[c16 * LDK + 16 * m + 4 * gq + i] = kt[j];
-        s_kb[c16 * LDK + 16 * m + 4 * gq + i] = Eb * xk[i];
+        s_kb[c16 * LDK + 16 * m + 4 * gq + i] = kh[j] * Eg;  // e^(gamma - Gamma_r) k
       }
     }
 #pragma unroll
@@ -334,17 +334,16 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
       for (int i = 0; i < 4; ++i) {
         const float x = (valid ? gate_decay<GATE>(xg[i]) : 0.f) * kLog2e;
         const float G = row_inclusive_prefix_sum(x);
-        const float Gb = row_exclusive_suffix_sum(x);
         const float E = __builtin_amdgcn_exp2f(G);
         const float Eh = __builtin_amdgcn_exp2f(-G);
-        const float Eb = __builtin_amdgcn_exp2f(Gb);
+        const float Eg = row_broadcast_last(E);  // e^gamma
         const int j = 4 * jj + i;
         const int ch = 16 * m + 4 * gq + i;
         qt[j] = E * xq[i];
         kt[j] = E * xk[i];
         kh[j] = Eh * xk[i];
         s_kt[w][c16 * LDK + ch] = static_cast<Op>(kt[j]);
-        s_kb[w][c16 * LDK + ch] = static_cast<Op>(Eb * xk[i]);
+        s_kb[w][c16 * LDK + ch] = static_cast<Op>(kh[j] * Eg);  // e^(gamma - Gamma_r) k
         if (w == 1) s_qt[c16 * LDK + ch] = static_cast<Op>(qt[j]);
         if (c16 == 15) s_eg[w][ch] = E;  // e^gamma: the decay to the chunk's end
       }

@@ -144,15 +144,9 @@ __device__ __forceinline__ float row_inclusive_prefix_sum(float x) {
   return x;
 }
 
-// Exclusive suffix sum over the row (lane r gets sum of lanes r+1..15).
-__device__ __forceinline__ float row_exclusive_suffix_sum(float x) {
-  float y = dpp_move<0x101>(x);  // row_shl:1
-  y += dpp_move<0x101>(y);
-  y += dpp_move<0x102>(y);
-  y += dpp_move<0x104>(y);
-  y += dpp_move<0x108>(y);
-  return y;
-}
+// Lane 15 of each row broadcast to the whole row (row_newbcast:15): the value
+// at a chunk's last token, e.g. e^gamma from e^Gamma_r.
+__device__ __forceinline__ float row_broadcast_last(float x) { return dpp_move<0x15F>(x); }
 
 // ---- MFMA wrappers (16x16 output tiles, fp32 accumulate) -----------------
 // Output layout for every 16x16 tile: lane l holds rows 4*(l/16)+i, i=0..3,

@@ -939,6 +939,13 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   if (wave < kLd) {
     // ---------------- loaders ----------------
     const bool has_v = wave == kLd - 1 && MODE != kPassTransition;
+    // The slice groups of a head read the same record lines in the same
+    // step. Each group starts its share of the units at a different place
+    // (unit u of this loader's share is taken in turn (u + rot) mod
+    // kUnitsPer), so that the groups' requests for a line do not arrive at
+    // the L2 together (64K-token workload, 32 heads: 1.51 against 1.55 ms).
+    static_assert(G::kUnits % kLd == 0, "every loader takes the same number of record units");
+    const int rot = static_cast<int>((2 * group) % G::kUnitsPer);
     // V: lane -> tokens 2a, 2a + 1 of the pair (a = 0..15), columns 4cq ..
     // 4cq + 3 of each slice of the group
     const int va = l & 15, cq = l >> 4;
@@ -953,8 +960,8 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       const uint8_t* src = rec0 + static_cast<size_t>(cc) * G::kRec;
 #pragma unroll
       for (int u = 0; u < G::kUnitsPer; ++u) {
-        const int j = wave + u * kLd;
-        if (j < G::kUnits) st.r[u] = ld_at<u32x4>(src, static_cast<uint32_t>(j * 64 + l) * 16);
+        const int j = wave + (u + rot) % G::kUnitsPer * kLd;
+        st.r[u] = ld_at<u32x4>(src, static_cast<uint32_t>(j * 64 + l) * 16);
       }
       if (has_v) {
         const int64_t tmax = T - 1 - cc * 32;
@@ -976,8 +983,8 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       uint8_t* dst = ring + static_cast<int>(c % kR) * G::kSlot;
 #pragma unroll
       for (int u = 0; u < G::kUnitsPer; ++u) {
-        const int j = wave + u * kLd;
-        if (j < G::kUnits) st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[u]);
+        const int j = wave + (u + rot) % G::kUnitsPer * kLd;
+        st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[u]);
       }
       if (has_v) {
         // V^T[col][token], the exact bf16 values, one tile per chunk of the

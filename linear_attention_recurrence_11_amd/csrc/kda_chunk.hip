@@ -72,6 +72,18 @@ __device__ __forceinline__ bf16x8 split_bf16(const float (&x)[4]) {
   return r;
 }
 
+// Eight bf16 values in 16 bytes, and their fp32 values. The type's alignment
+// is the inputs' documented 8 bytes; the hardware serves a 16-byte vector load
+// from any dword-aligned address.
+typedef uint32_t u32x4a8 __attribute__((ext_vector_type(4), aligned(8)));
+__device__ __forceinline__ void unpack8(const u32x4a8& x, float out[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    out[2 * d] = __uint_as_float(x[d] << 16);
+    out[2 * d + 1] = __uint_as_float(x[d] & 0xffff0000u);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Record fragment addressing. Each lane's values come in groups of 4
 // consecutive rows/tokens i = 0..3.
@@ -279,12 +291,12 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
                                                            uint8_t* __restrict__ ws, int64_t T,
                                                            int64_t H, int64_t NPR, PairLayout L) {
   constexpr int NM = DK / 16;
-  constexpr int LDK = DK + 4;  // padded LDS row (conflict-free transposed reads)
+  constexpr int LDK = DK + 8;  // padded LDS row: 16-byte aligned, conflict-free transposed reads
   using Op = _Float16;
   __shared__ float s_beta[2][16];
-  __shared__ Op s_kt[2][16 * LDK];
-  __shared__ Op s_kb[2][16 * LDK];
-  __shared__ Op s_qt[16 * LDK];       // Qt of c2 (before the e^g1 factor)
+  __shared__ __attribute__((aligned(16))) Op s_kt[2][16 * LDK];
+  __shared__ __attribute__((aligned(16))) Op s_kb[2][16 * LDK];
+  __shared__ __attribute__((aligned(16))) Op s_qt[2][16 * LDK];  // Qt of each chunk (before the e^g1 factor)
   __shared__ float s_eg[2][DK];       // e^gamma of each chunk, per channel
   __shared__ float s_A[2][16][17];
   __shared__ float s_T[2][16][17];
@@ -301,55 +313,51 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
   const size_t tok = static_cast<size_t>((b * T + (valid ? t : 0)) * H + h);
   uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NPR + sp) * L.bytes;
 
-  // ---- loads, kept packed until used ----
-  uint2 rq[NM], rk[NM], rg[NM];
+  // ---- loads, kept packed until used: 8 consecutive channels per lane ----
+  u32x4a8 rq[NM / 2], rk[NM / 2], rg[NM / 2];
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const size_t off = tok * DK + 16 * m + 4 * gq;
+  for (int p = 0; p < NM / 2; ++p) {
+    const size_t off = tok * DK + 32 * p + 8 * gq;
     if (valid) {
-      rq[m] = *reinterpret_cast<const uint2*>(q + off);
-      rk[m] = *reinterpret_cast<const uint2*>(k + off);
-      rg[m] = *reinterpret_cast<const uint2*>(g + off);
+      rq[p] = *reinterpret_cast<const u32x4a8*>(q + off);
+      rk[p] = *reinterpret_cast<const u32x4a8*>(k + off);
+      rg[p] = *reinterpret_cast<const u32x4a8*>(g + off);
     } else {
-      rq[m] = rk[m] = rg[m] = uint2{};
+      rq[p] = rk[p] = rg[p] = u32x4a8{0u, 0u, 0u, 0u};
     }
   }
   if (gq == 0) s_beta[w][c16] = valid ? load_in(beta, tok) : 0.f;
 
-  // ---- per pair of 16-channel groups: decay scan, scaled operands, Gram ----
-  // (as in kda_chunk_prep; channel (m, i) = 16m + 4gq + i, Gram slot
-  // j = 4(m - 2p) + i)
+  // ---- per 32 channels: decay scan, scaled operands, Gram (channel
+  // 32p + 8gq + i is Gram slot i of the lane) ----
   f32x4 Araw = zero4(), MrawT = zero4();
 #pragma unroll
   for (int p = 0; p < NM / 2; ++p) {
-    float qt[8], kt[8], kh[8];
+    float qt[8], kt[8], kh[8], xq[8], xk[8], xg[8];
+    unpack8(rq[p], xq);
+    unpack8(rk[p], xk);
+    unpack8(rg[p], xg);
+    f16x8 kt16, kb16, qt16;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int m = 2 * p + jj;
-      float xq[4], xk[4], xg[4];
-      unpack4(rq[m], xq);
-      unpack4(rk[m], xk);
-      unpack4(rg[m], xg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = (valid ? gate_decay<GATE>(xg[i]) : 0.f) * kLog2e;
-        const float G = row_inclusive_prefix_sum(x);
-        const float E = __builtin_amdgcn_exp2f(G);
-        const float Eh = __builtin_amdgcn_exp2f(-G);
-        const float Eg = row_broadcast_last(E);  // e^gamma
-        const int j = 4 * jj + i;
-        const int ch = 16 * m + 4 * gq + i;
-        qt[j] = E * xq[i];
-        kt[j] = E * xk[i];
-        kh[j] = Eh * xk[i];
-        s_kt[w][c16 * LDK + ch] = static_cast<Op>(kt[j]);
-        s_kb[w][c16 * LDK + ch] = static_cast<Op>(kh[j] * Eg);  // e^(gamma - Gamma_r) k
-        if (w == 1) s_qt[c16 * LDK + ch] = static_cast<Op>(qt[j]);
-        if (c16 == 15) s_eg[w][ch] = E;  // e^gamma: the decay to the chunk's end
-      }
+    for (int i = 0; i < 8; ++i) {
+      const float x = (valid ? gate_decay<GATE>(xg[i]) : 0.f) * kLog2e;
+      const float G = row_inclusive_prefix_sum(x);
+      const float E = __builtin_amdgcn_exp2f(G);
+      const float Eh = __builtin_amdgcn_exp2f(-G);
+      const float Eg = row_broadcast_last(E);  // e^gamma
+      qt[i] = E * xq[i];
+      kt[i] = E * xk[i];
+      kh[i] = Eh * xk[i];
+      kt16[i] = static_cast<Op>(kt[i]);
+      kb16[i] = static_cast<Op>(kh[i] * Eg);  // e^(gamma - Gamma_r) k
+      qt16[i] = static_cast<Op>(qt[i]);
+      if (c16 == 15) s_eg[w][32 * p + 8 * gq + i] = E;  // e^gamma: the decay to the chunk's end
     }
+    const int row = c16 * LDK + 32 * p + 8 * gq;  // one 16-byte store per lane and tile
+    *reinterpret_cast<f16x8*>(&s_kt[w][row]) = kt16;
+    *reinterpret_cast<f16x8*>(&s_kb[w][row]) = kb16;
+    *reinterpret_cast<f16x8*>(&s_qt[w][row]) = qt16;
     bf16x8 kt_hi, kt_lo, kh_hi, kh_lo, qt_hi, qt_lo;
-    f16x8 qv;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       kt_hi[j] = static_cast<__bf16>(kt[j]);
@@ -358,7 +366,6 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
       kh_lo[j] = static_cast<__bf16>(kh[j] - static_cast<float>(kh_hi[j]));
       qt_hi[j] = static_cast<__bf16>(qt[j]);
       qt_lo[j] = static_cast<__bf16>(qt[j] - static_cast<float>(qt_hi[j]));
-      qv[j] = static_cast<Op>(qt[j]);
     }
     Araw = mma_16x16x32_bf16(kt_hi, kh_hi, Araw);
     Araw = mma_16x16x32_bf16(kt_hi, kh_lo, Araw);
@@ -366,9 +373,19 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
     MrawT = mma_16x16x32_bf16(kh_hi, qt_hi, MrawT);
     MrawT = mma_16x16x32_bf16(kh_lo, qt_hi, MrawT);
     MrawT = mma_16x16x32_bf16(kh_hi, qt_lo, MrawT);
-    if (w == 0) *reinterpret_cast<f16x8*>(rec + L.q1 + static_cast<size_t>(p * 64 + l) * 16) = qv;
   }
   __syncthreads();  // s_beta, s_kt, s_kb, s_qt, s_eg of both chunks visible
+  if (w == 0) {
+    // Qt of c1 in the record's fragment order (channel 16m + 4gq + i of the
+    // lane's token), read back from LDS
+#pragma unroll
+    for (int p = 0; p < NM / 2; ++p) {
+      f16x8 qv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = s_qt[0][c16 * LDK + 16 * (2 * p + (j >> 2)) + 4 * gq + (j & 3)];
+      *reinterpret_cast<f16x8*>(rec + L.q1 + static_cast<size_t>(p * 64 + l) * 16) = qv;
+    }
+  }
 
   // ---- mask: A strictly lower with row scale beta_r ----
 #pragma unroll
@@ -460,7 +477,7 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
         const int ch = 16 * m + 4 * gq + i;
         kb1[j] = s_kb[0][c16 * LDK + ch];
         w2[j] = static_cast<Op>(wv[m][i]);
-        q2[j] = s_qt[c16 * LDK + ch];
+        q2[j] = s_qt[1][c16 * LDK + ch];
       }
       C21T = mma_16x16x32_f16(kb1, w2, C21T);
       M21T = mma_16x16x32_f16(kb1, q2, M21T);
@@ -476,7 +493,7 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
         const int ch = 16 * m + 4 * gq + i;
         const float e1 = eg1[ch];
         x[j] = static_cast<Op>(-wv[m][i] * e1);
-        y[j] = static_cast<Op>(static_cast<float>(s_qt[c16 * LDK + ch]) * e1);
+        y[j] = static_cast<Op>(static_cast<float>(s_qt[1][c16 * LDK + ch]) * e1);
       }
       *reinterpret_cast<f16x8*>(rec + L.w2 + static_cast<size_t>(p * 64 + l) * 16) = x;
       *reinterpret_cast<f16x8*>(rec + L.q2 + static_cast<size_t>(p * 64 + l) * 16) = y;

@@ -132,6 +132,27 @@ def test_split_resume(dt):
     assert rel_err(S2.cpu().numpy(), ST.cpu().numpy()) <= tol
 
 
+@pytest.mark.parametrize("dk", [64, 128])
+def test_bf16_inputs_at_the_minimum_alignment(dk):
+    """q, k and g 8 bytes off a 16-byte boundary (their documented alignment
+    is 4 elements; the prep reads them as 16-byte vectors): the same outputs,
+    bit for bit, as from 16-byte-aligned copies."""
+    B, T, H, dv = 2, 100, 3, 64
+    ins = inputs.make_forward(B, T, H, dk, dv, "bf16", "normal", seed=61 + dk, device=DEV)
+    announce("8-byte-aligned bf16 inputs, dk", dk)
+    o_ref, S_ref = gpu_forward(ins)
+    shifted = {}
+    for n in ("q", "k", "g"):
+        x = ins[n]
+        buf = torch.empty(x.numel() + 8, dtype=x.dtype, device=DEV)
+        y = buf[4:4 + x.numel()].view(x.shape)
+        y.copy_(x)
+        assert y.data_ptr() % 16 == 8
+        shifted[n] = y
+    o, S = gpu_forward(dict(ins, **shifted))
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
 def test_in_place_state_and_empty():
     ins = inputs.make_forward(1, 50, 2, 64, 64, "bf16", "normal", seed=17, device=DEV)
     announce("in-place state; T=0")

@@ -175,6 +175,29 @@ def test_large_values_bf16(dk, dv):
     assert rel_err(sn[:, 3].cpu().numpy(), S_pre) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B", [4, 8], ids=["2_slices", "4_slices"])
+def test_large_values_in_multi_slice_workgroups(B):
+    """Large values where the plain pass serves 2 or 4 slices per workgroup
+    (512 and 1024 slices of 128 x 128 heads): slices whose fp16 operands
+    overflow there raise their range flag, and the scaled pass (one slice per
+    workgroup) redoes them. Only the even heads get the large v, so flagged
+    and unflagged slices mix."""
+    T, H, dk, dv = 96, 16, 128, 128
+    announce("large values, multi-slice workgroups, B", B)
+    ins = inputs.make_forward(B, T, H, dk, dv, "bf16", "normal", seed=84 + B, device=DEV)
+    v = ins["v"].float()
+    v[:, :, ::2] *= 3e4   # even heads
+    ins["v"] = v.to(torch.bfloat16)
+    ins["S0"] = ins["S0"] * (1e3 / 0.02)
+    o, ST = gpu_forward(ins)
+    o_ref, S_ref = oracle_forward(ins)
+    for hs in (slice(0, None, 2), slice(1, None, 2)):   # each group of heads on its own scale
+        eo = rel_err(o[:, :, hs].cpu().numpy(), o_ref[:, :, hs])
+        es = rel_err(ST[:, hs].cpu().numpy(), S_ref[:, hs])
+        announce("  heads %s: err_o=%.3g err_S=%.3g" % (hs, eo, es))
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_values_jump_by_twelve_orders_and_back():
     """A burst of values near 1e12 in the middle of a sequence, then 64 tokens
     at the -5 floor that forget it, then ordinary values again: the outputs

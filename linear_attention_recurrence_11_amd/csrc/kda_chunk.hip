@@ -28,14 +28,16 @@
 //               applies the lines that couple chunks, in order. Columns of S
 //               never interact, so slices need no communication.
 // fp32 inputs use fp32 matrix cores, one record per chunk (kda_chunk_prep,
-// kda_state_pass). bf16 inputs use fp16 operands, one record per pair of
-// chunks, and the state pass advances 32 tokens per step
-// (kda_chunk_prep_pair, kda_state_pass_ring32).
+// kda_state_pass). bf16 inputs use fp16 operands for the state products (v
+// stays exact in bf16 products), one record per pair of chunks, and the state
+// pass advances 32 tokens per step (kda_chunk_prep_pair,
+// kda_state_pass_ring32).
 //
 // Lane conventions (l = lane, c16 = l % 16, gq = l / 16): a 16x16 MFMA output
 // tile has lane l holding rows 4*gq + i (i = 0..3) of column c16. In the prep
-// kernel lane l owns token c16 and key channels 16*m + 4*gq + i of it; the
-// contraction slots of every dk-contraction are mapped to channels so that the
+// kernels lane l owns token c16 (key channels 16*m + 4*gq + i of it in the
+// fp32 prep, 32*p + 8*gq + i in the pair prep); the records' contraction slots
+// of every dk-contraction are mapped to channels 16*m + 4*gq + i, so that the
 // state slice, held in output layout, is directly the B operand of W S and
 // Qt S (no shuffles on the sequential path).
 #include <mutex>
@@ -772,9 +774,10 @@ __global__ __launch_bounds__(64) void kda_state_pass(const float* __restrict__ v
 // compute wave pads its barrier count to match.
 //
 // Per step the compute wavefront evaluates the pair lines of
-// kda_chunk_prep_pair: 29 16x16x32 MFMAs, one decay multiply and one fp16
-// conversion of its state slice, two output stores and one barrier, against
-// 36 MFMAs and two of each of the rest for two 16-token steps.
+// kda_chunk_prep_pair: 30 16x16x32 MFMAs (two of them bf16, for v's exact
+// product), one decay multiply and one fp16 conversion of its state slice,
+// two output stores and one barrier, against 36 MFMAs and two of each of the
+// rest for two 16-token steps.
 // ---------------------------------------------------------------------------
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

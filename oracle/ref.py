@@ -18,6 +18,10 @@ chunked  the same result reached chunk by chunk, written out matrix by matrix
            U = Ut - W S0,  O = Qt S0 + M U,  S_C = Diag(e^gamma) S0 + Kb^T U
          A last chunk shorter than C is just a shorter chunk.
 
+chunk_terms
+         one chunk's matrices of that form (used by chunked, and by tests of
+         the prepared per-chunk operands).
+
 affine_scan
          the states entering consecutive spans of a sequence from each span's
          affine map S_out = F S_in + E (F: the span's state transition, the
@@ -54,6 +58,25 @@ def seq(q, k, v, g, beta, S0=None):
     return o, S
 
 
+def chunk_terms(q, k, g, beta):
+    """The chunk form's per-chunk matrices for one chunk of n tokens (q, k, g
+    [n, dk], beta [n]; g already clamped): Gam, gam, Qt, Kt, Kh, Kb, A, M,
+    Tm, W and Tb = Tm diag(beta), in the notation of the module docstring."""
+    n = q.shape[0]
+    Gam = np.cumsum(g, axis=0)
+    gam = Gam[-1]
+    Qt = np.exp(Gam) * q
+    Kt = np.exp(Gam) * k
+    Kh = np.exp(-Gam) * k
+    Kb = np.exp(gam[None, :] - Gam) * k
+    A = np.tril(beta[:, None] * (Kt @ Kh.T), -1)
+    M = np.tril(Qt @ Kh.T)
+    Tm = np.linalg.inv(np.eye(n) + A)
+    W = Tm @ (beta[:, None] * Kt)
+    return dict(Gam=Gam, gam=gam, Qt=Qt, Kt=Kt, Kh=Kh, Kb=Kb, A=A, M=M, Tm=Tm, W=W,
+                Tb=Tm * beta[None, :])
+
+
 def chunked(q, k, v, g, beta, S0=None, C=16):
     q, k, v, beta = (np.asarray(x, np.float64) for x in (q, k, v, beta))
     g = clamp_decay(g)
@@ -63,21 +86,11 @@ def chunked(q, k, v, g, beta, S0=None, C=16):
     o = np.empty((T, dv))
     for start in range(0, T, C):
         sl = slice(start, min(start + C, T))
-        n = sl.stop - sl.start
-        Gam = np.cumsum(g[sl], axis=0)
-        gam = Gam[-1]
-        Qt = np.exp(Gam) * q[sl]
-        Kt = np.exp(Gam) * k[sl]
-        Kh = np.exp(-Gam) * k[sl]
-        Kb = np.exp(gam[None, :] - Gam) * k[sl]
-        A = np.tril(beta[sl][:, None] * (Kt @ Kh.T), -1)
-        M = np.tril(Qt @ Kh.T)
-        Tm = np.linalg.inv(np.eye(n) + A)
-        W = Tm @ (beta[sl][:, None] * Kt)
-        Ut = Tm @ (beta[sl][:, None] * v[sl])
-        U = Ut - W @ S
-        o[sl] = Qt @ S + M @ U
-        S = np.exp(gam)[:, None] * S + Kb.T @ U
+        c = chunk_terms(q[sl], k[sl], g[sl], beta[sl])
+        Ut = c["Tb"] @ v[sl]
+        U = Ut - c["W"] @ S
+        o[sl] = c["Qt"] @ S + c["M"] @ U
+        S = np.exp(c["gam"])[:, None] * S + c["Kb"].T @ U
     return o, S
 
 

@@ -24,10 +24,10 @@
 // load the next unit's state while replaying the current one (spec_threads,
 // kCommitGrid). Thread t owns float4 column group cg = t % (dv/4) of rows
 // rg + RG*j, as in the decode step, and keeps its part of S in registers
-// across all tokens. Per token three
-// barriers: token inputs staged, partial reductions written, u published.
-// The token inputs are double-buffered by token parity so that the next
-// token's staging cannot overwrite what slower threads still read.
+// across all tokens. The inputs of up to kTokBlock tokens are staged in LDS
+// at once, loaded together (in verify, while the state loads are in flight),
+// so no token waits on a global load of its own. Per token two barriers:
+// partial reductions written, u published.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -45,9 +45,18 @@ constexpr int spec_threads() {
   return COMMIT ? 1024 : 256;
 }
 constexpr int64_t kCommitGrid = 1024;
+constexpr int kTokBlock = 8;  // tokens whose inputs are staged in LDS at once
+
+// Wavefronts per SIMD the register allocation must leave room for: verify
+// relies on several resident workgroups hiding each other's latency.
+template <bool COMMIT>
+constexpr int spec_waves_per_simd() {
+  return COMMIT ? 1 : 4;
+}
 
 template <typename InT, typename OutT, int DK, int DV, int GATE, bool COMMIT>
-__global__ __launch_bounds__(spec_threads<COMMIT>()) void kda_spec_kernel(const InT* __restrict__ q,
+__global__ __launch_bounds__(spec_threads<COMMIT>()) __attribute__((amdgpu_waves_per_eu(spec_waves_per_simd<COMMIT>())))
+void kda_spec_kernel(const InT* __restrict__ q,
                                                        const InT* __restrict__ k,
                                                        const InT* __restrict__ v,
                                                        const InT* __restrict__ g,
@@ -61,10 +70,11 @@ __global__ __launch_bounds__(spec_threads<COMMIT>()) void kda_spec_kernel(const 
   constexpr int RG = NT / CPR;
   constexpr int RPT = DK / RG;
   static_assert(RPT >= 1 && DK % RG == 0, "shape");
-  __shared__ float s_q[2][DK], s_k[2][DK], s_e[2][DK];
-  __shared__ float s_red[2][RG][DV + 4];
+  constexpr int TB = kTokBlock, NW = NT / 64;
+  __shared__ float s_q[COMMIT ? 1 : TB][DK], s_k[TB][DK], s_e[TB][DK], s_v[TB][DV];
+  __shared__ float s_b[TB], s_qk[TB];
+  __shared__ float s_red[COMMIT ? 1 : 2][RG][DV + 4];
   __shared__ float s_u[DV];
-  __shared__ float s_qk;
 
   const int t = threadIdx.x;
   const int cg = t % CPR, rg = t / CPR;
@@ -102,60 +112,73 @@ __global__ __launch_bounds__(spec_threads<COMMIT>()) void kda_spec_kernel(const 
       const int64_t a = accepted[n];
       ntok = a < 0 ? 0 : (a > T ? T : a);
     }
-    __syncthreads();  // the previous unit's LDS readers are done
-    for (int64_t tt = 0; tt < ntok; ++tt) {
-      const int pb = static_cast<int>(tt & 1);
-      const size_t tok = static_cast<size_t>((n * T + tt) * H + h);
-      for (int i = t; i < DK; i += NT) {
-        if constexpr (!COMMIT) s_q[pb][i] = load_in(q, tok * DK + i);
-        s_k[pb][i] = load_in(k, tok * DK + i);
-        s_e[pb][i] = expf(gate_decay<GATE>(load_in(g, tok * DK + i)));
+    for (int64_t t0 = 0; t0 < ntok; t0 += TB) {
+      const int nb = static_cast<int>(ntok - t0 < TB ? ntok - t0 : TB);
+      const size_t tok0 = static_cast<size_t>((n * T + t0) * H + h);  // token j: tok0 + j * H
+      __syncthreads();  // the readers of the previous block (or unit) are done
+      for (int i = t; i < nb * DK; i += NT) {
+        const int j = i / DK, c = i % DK;
+        const size_t x = (tok0 + static_cast<size_t>(j) * H) * DK + c;
+        if constexpr (!COMMIT) s_q[j][c] = load_in(q, x);
+        s_k[j][c] = load_in(k, x);
+        s_e[j][c] = expf(gate_decay<GATE>(load_in(g, x)));
       }
+      for (int i = t; i < nb * DV; i += NT) {
+        const int j = i / DV, c = i % DV;
+        s_v[j][c] = load_in(v, (tok0 + static_cast<size_t>(j) * H) * DV + c);
+      }
+      if (t < nb) s_b[t] = load_in(beta, tok0 + static_cast<size_t>(t) * H);
       __syncthreads();
       if constexpr (!COMMIT) {
-        if (t < 64) {
+        // q_t . k_t of each token, one wavefront per token; read after the
+        // token's first barrier
+        const int w = t >> 6, l = t & 63;
+        for (int j = w; j < nb; j += NW) {
           float acc = 0.f;
-          for (int i = t; i < DK; i += 64) acc += s_q[pb][i] * s_k[pb][i];
+          for (int c = l; c < DK; c += 64) acc += s_q[j][c] * s_k[j][c];
 #pragma unroll
           for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-          if (t == 0) s_qk = acc;
+          if (l == 0) s_qk[j] = acc;
         }
       }
-      float r4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < nb; ++j) {
+        float r4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        const int row = rg + RG * j;
-        const float e = s_e[pb][row], kr = s_k[pb][row];
-        s[j].x *= e; s[j].y *= e; s[j].z *= e; s[j].w *= e;
-        r4[0] += kr * s[j].x; r4[1] += kr * s[j].y; r4[2] += kr * s[j].z; r4[3] += kr * s[j].w;
-        if constexpr (!COMMIT) {
-          const float qr = s_q[pb][row];
-          p4[0] += qr * s[j].x; p4[1] += qr * s[j].y; p4[2] += qr * s[j].z; p4[3] += qr * s[j].w;
+        for (int jj = 0; jj < RPT; ++jj) {
+          const int row = rg + RG * jj;
+          const float e = s_e[j][row], kr = s_k[j][row];
+          s[jj].x *= e; s[jj].y *= e; s[jj].z *= e; s[jj].w *= e;
+          r4[0] += kr * s[jj].x; r4[1] += kr * s[jj].y; r4[2] += kr * s[jj].z; r4[3] += kr * s[jj].w;
+          if constexpr (!COMMIT) {
+            const float qr = s_q[j][row];
+            p4[0] += qr * s[jj].x; p4[1] += qr * s[jj].y; p4[2] += qr * s[jj].z; p4[3] += qr * s[jj].w;
+          }
         }
-      }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s_red[0][rg][4 * cg + c] = r4[c];
-        if constexpr (!COMMIT) s_red[1][rg][4 * cg + c] = p4[c];
-      }
-      __syncthreads();
-      if (t < DV) {
-        float r = 0.f, p = 0.f;
-#pragma unroll
-        for (int x = 0; x < RG; ++x) {
-          r += s_red[0][x][t];
-          if constexpr (!COMMIT) p += s_red[1][x][t];
+        for (int c = 0; c < 4; ++c) {
+          s_red[0][rg][4 * cg + c] = r4[c];
+          if constexpr (!COMMIT) s_red[COMMIT ? 0 : 1][rg][4 * cg + c] = p4[c];
         }
-        const float u = load_in(beta, tok) * (load_in(v, tok * DV + t) - r);
-        s_u[t] = u;
-        if constexpr (!COMMIT) store_out(o, tok * DV + t, p + s_qk * u);
-      }
-      __syncthreads();
-      const float u0 = s_u[4 * cg], u1 = s_u[4 * cg + 1], u2 = s_u[4 * cg + 2], u3 = s_u[4 * cg + 3];
+        __syncthreads();
+        if (t < DV) {
+          float r = 0.f, p = 0.f;
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        const float kr = s_k[pb][rg + RG * j];
-        s[j].x += kr * u0; s[j].y += kr * u1; s[j].z += kr * u2; s[j].w += kr * u3;
+          for (int x = 0; x < RG; ++x) {
+            r += s_red[0][x][t];
+            if constexpr (!COMMIT) p += s_red[COMMIT ? 0 : 1][x][t];
+          }
+          const float u = s_b[j] * (s_v[j][t] - r);
+          s_u[t] = u;
+          if constexpr (!COMMIT)
+            store_out(o, (tok0 + static_cast<size_t>(j) * H) * DV + t, p + s_qk[j] * u);
+        }
+        __syncthreads();
+        const float u0 = s_u[4 * cg], u1 = s_u[4 * cg + 1], u2 = s_u[4 * cg + 2], u3 = s_u[4 * cg + 3];
+#pragma unroll
+        for (int jj = 0; jj < RPT; ++jj) {
+          const float kr = s_k[j][rg + RG * jj];
+          s[jj].x += kr * u0; s[jj].y += kr * u1; s[jj].z += kr * u2; s[jj].w += kr * u3;
+        }
       }
     }
     if constexpr (COMMIT) {

@@ -173,6 +173,35 @@ def test_spec_commit_replays_the_accepted_prefix(dt):
         assert e <= 1e-4, (n, a, e)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_spec_many_drafts_cross_token_blocks(dt, dk, dv):
+    # 19 drafts: the kernels stage the inputs of 8 tokens at a time, so this
+    # runs blocks of 8, 8 and 3; accepted counts end inside, at and next to
+    # block edges
+    N, T, H = 8, 19, 2
+    announce("spec many drafts", dt, dk, dv)
+    ins = _spec_inputs(N, T, H, dk, dv, dt, seed=71 + dk)
+    o = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"])
+    acc_list = [0, 7, 8, 9, 16, 19, 3, 17]
+    accepted = torch.tensor(acc_list, dtype=torch.int32, device=DEV)
+    S = ins["S0"].clone()
+    binding.kda_spec_commit(ins["k"], ins["v"], ins["g"], ins["beta"], S, accepted)
+    torch.cuda.synchronize()
+    o_ref, _ = _oracle(ins)
+    e = rel_err(o.cpu().numpy(), o_ref)
+    announce("err_o %.3g" % e)
+    assert e <= 1e-4
+    for n, a in enumerate(acc_list):
+        if a == 0:
+            assert torch.equal(S[n], ins["S0"][n])
+            continue
+        one = {m: ins[m][n:n + 1, :a].contiguous() for m in ("q", "k", "v", "g", "beta")}
+        one["S0"] = ins["S0"][n:n + 1]
+        _, S_ref = _oracle(one)
+        assert rel_err(S[n].cpu().numpy(), S_ref[0]) <= 1e-4, (n, a)
+
+
 def test_spec_commit_more_units_than_workgroups():
     # 41 x 26 = 1066 units against at most 1024 persistent workgroups, with
     # a different accepted count per request (zero included): the prefetch

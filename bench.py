@@ -49,6 +49,61 @@ def prefill_units(dk, dv, in_bytes=2, C=16):
     return flops, bytes_
 
 
+class ClockSampler:
+    """The shader clock during the timed steps, as the driver reports it: the
+    current level of pp_dpm_sclk (the line marked '*'), read from sysfs every
+    few milliseconds by a background thread. Reads a file only; never touches
+    the GPU. None where the file is missing or unreadable."""
+
+    PERIOD_S = 0.005
+
+    def __init__(self):
+        import glob
+        self.path = next((p for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+                          if os.access(p, os.R_OK)), None)
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def start(self):
+        if self.path is None:
+            return
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                mhz = self._read()
+                if mhz is not None:
+                    self.samples.append(mhz)
+                self._stop.wait(self.PERIOD_S)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"source": self.path.replace("/device/pp_dpm_sclk", "") + " pp_dpm_sclk (current level)",
+                "samples": len(xs), "min_mhz": xs[0], "median_mhz": xs[len(xs) // 2],
+                "max_mhz": xs[-1], "peak_mhz": 2400}
+
+
 def source_sha(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -149,12 +204,15 @@ def main():
 
     log("timing %d steps" % args.steps)
     all_ev = [new_events() for _ in range(args.steps)]
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(all_ev[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gpu_clock = clock.stop()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     prep_ms = np.array([e[0].elapsed_time(e[1]) for e in all_ev])
@@ -233,6 +291,7 @@ def main():
                    "decode_workload": dc.name, "decode_requests": N, "decode_steps": steps},
         "roofline": roofs[dominant],
         "roofline_prefill": roof_prefill,
+        "gpu_clock_during_timed_steps": gpu_clock,
         "roofline_decode": r_dec,
         "prefill": {
             "tokens_per_s": round(value, 1), "ms": round(prefill_ms.mean(), 4),

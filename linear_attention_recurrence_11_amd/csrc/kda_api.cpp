@@ -100,8 +100,10 @@ kda_status check_chunk(const ChunkPtrs& p, int64_t B, int64_t T, int64_t H, int6
   if (dv < 16 || dv > 512 || dv % 16 != 0) return KDA_ERR_UNSUPPORTED;
   const double toks = static_cast<double>(B) * T * H;
   if (toks * (dk > dv ? dk : dv) > static_cast<double>(kMaxElems)) return KDA_ERR_SHAPE;
+  // B * H first, in double: with T = 0 the token bound above admits any B, H
+  if (static_cast<double>(B) * H > static_cast<double>(0x0fffffffLL)) return KDA_ERR_UNSUPPORTED;
   const int64_t NC = (T + 15) / 16;
-  if (B * H * NC > 0x7fffffffLL || B * H > 0x0fffffffLL) return KDA_ERR_UNSUPPORTED;
+  if (B * H * NC > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
   if (H * dv > (int64_t(1) << 25)) return KDA_ERR_UNSUPPORTED;  // 32-bit per-lane offsets
   const int64_t BH = B * H, BTH = B * T * H;
   if (BH == 0) return KDA_OK;  // nothing to read or write
@@ -404,8 +406,10 @@ kda_status check_transition(const void* v, const void* ws, size_t ws_bytes, cons
   if (dv < 16 || dv > 512 || dv % 16 != 0) return KDA_ERR_UNSUPPORTED;
   const double toks = static_cast<double>(B) * T * H;
   if (toks * (dk > dv ? dk : dv) > static_cast<double>(kMaxElems)) return KDA_ERR_SHAPE;
+  // B * H first, in double: with T = 0 the token bound above admits any B, H
+  if (static_cast<double>(B) * H > static_cast<double>(0x0fffffffLL)) return KDA_ERR_UNSUPPORTED;
   const int64_t NC = (T + 15) / 16;
-  if (B * H * NC > 0x7fffffffLL || B * H > 0x0fffffffLL) return KDA_ERR_UNSUPPORTED;
+  if (B * H * NC > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
   if (H * (dk > dv ? dk : dv) > (int64_t(1) << 25)) return KDA_ERR_UNSUPPORTED;
   const int64_t BH = B * H;
   if (BH == 0) return KDA_OK;

@@ -134,6 +134,18 @@ def test_chunk_empty_needs_nothing(lib):
     assert check(lib, p, (0, T, H, dk, dv, ind, outd), **nulls) == OK
 
 
+def test_chunk_empty_sequence_with_huge_batch_and_heads(lib):
+    # T = 0 puts no bound on B and H through the token count; B * H = 2^80
+    # must be rejected without forming the product in 64-bit integers
+    p, sz = fake_chunk()
+    B, T, H, dk, dv, ind, outd = sz
+    nulls = dict(q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, ws_bytes=0,
+                 S0=None, S_T=None)
+    assert check(lib, p, (1 << 40, 0, 1 << 40, dk, dv, ind, outd), **nulls) == UNSUP
+    assert check(lib, p, (1 << 14, 0, 1 << 14, dk, dv, ind, outd), **nulls) == UNSUP  # 2^28
+    assert check(lib, p, (1 << 13, 0, 1 << 14, dk, dv, ind, outd), **nulls) == OK
+
+
 def test_chunk_fwd_rejects_before_any_launch(lib):
     """kda_chunk_fwd returns the check's error without touching the GPU."""
     p, sz = fake_chunk()

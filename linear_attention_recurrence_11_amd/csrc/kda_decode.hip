@@ -15,10 +15,11 @@
 // instruction of a wavefront covers whole 512-byte rows (coalesced). At d =
 // 128 a thread holds four rows' float4: the 64 KiB state streams through
 // sixteen wavefronts at once, and the next unit's state is loaded while the
-// current one is reduced, updated and written back. Measured on 256
-// requests x 32 heads: 184.4 us per step with a grid of 1024 workgroups;
-// one workgroup per unit without the prefetch took 188.6 us, and 128-, 256-
-// or 512-thread workgroups took 195 us.
+// current one is reduced, updated and written back, together with that
+// unit's token inputs. Measured on 256 requests x 32 heads: 181.6 us per
+// step; 194 us with the inputs loaded after the next state's prefetch (their
+// use then waited for it), 188.6 us with one workgroup per unit and no
+// prefetch, 195 us with 128-, 256- or 512-thread workgroups.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -58,21 +59,44 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_kernel(const InT* __re
       x[j] = __builtin_nontemporal_load(
           reinterpret_cast<const f32x4*>(Su + static_cast<size_t>(rg + RG * j) * DV + 4 * cg));
   };
+  // The token inputs travel with the state: each unit's q, k, g (thread t <
+  // dk holds channel t) and v, beta (thread t < dv holds column t) are loaded
+  // one unit ahead, beside its state, and kept as loaded (bf16 bits) until
+  // used. Loads complete in order, so an input load issued after the next
+  // state's prefetch would make its first use wait for that whole prefetch.
+  static_assert(DK <= kDecThreads && DV <= kDecThreads, "one input element per thread");
+  InT nq{}, nk{}, ng{}, nv{}, nb{};
+  auto load_inputs = [&](int64_t u) __attribute__((always_inline)) {
+    if (t < DK) {
+      nq = q[u * DK + t];
+      nk = k[u * DK + t];
+      ng = g[u * DK + t];
+    }
+    if (t < DV) {
+      nv = v[u * DV + t];
+      nb = beta[u];
+    }
+  };
   f32x4 next[RPT];
   int64_t unit = blockIdx.x;  // the grid never exceeds the unit count
   load_state(unit, next);
+  load_inputs(unit);
   for (; unit < units; unit += stride) {  // uniform per workgroup
     float* Su = S + static_cast<size_t>(unit) * DK * DV;
     float4 s[RPT];
 #pragma unroll
     for (int j = 0; j < RPT; ++j) s[j] = make_float4(next[j][0], next[j][1], next[j][2], next[j][3]);
-    if (unit + stride < units) load_state(unit + stride, next);
+    const InT cq = nq, ck = nk, cgt = ng, cv = nv, cb = nb;
+    if (unit + stride < units) {
+      load_state(unit + stride, next);
+      load_inputs(unit + stride);
+    }
 
     __syncthreads();  // the previous unit's readers of s_q, s_k, s_e, s_u are done
-    for (int i = t; i < DK; i += kDecThreads) {
-      s_q[i] = load_in(q, unit * DK + i);
-      s_k[i] = load_in(k, unit * DK + i);
-      s_e[i] = expf(gate_decay<GATE>(load_in(g, unit * DK + i)));
+    if (t < DK) {
+      s_q[t] = to_f32(cq);
+      s_k[t] = to_f32(ck);
+      s_e[t] = expf(gate_decay<GATE>(to_f32(cgt)));
     }
     __syncthreads();
     if (t < 64) {  // q . k by one wavefront
@@ -106,7 +130,7 @@ __global__ __launch_bounds__(kDecThreads) void kda_decode_kernel(const InT* __re
         r += s_red[0][x][t];
         p += s_red[1][x][t];
       }
-      const float u = load_in(beta, unit) * (load_in(v, unit * DV + t) - r);
+      const float u = to_f32(cb) * (to_f32(cv) - r);
       s_u[t] = u;
       store_out(o, unit * DV + t, p + s_qk * u);
     }

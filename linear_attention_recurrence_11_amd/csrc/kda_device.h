@@ -35,6 +35,10 @@ template <> __device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p
   return bf16_bits_to_f32(p[i]);
 }
 
+// An input element as loaded (float, or bf16 bits) -> float.
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t b) { return bf16_bits_to_f32(b); }
+
 // Four consecutive input elements starting at p[i] (i a multiple of 4).
 template <typename T> __device__ __forceinline__ void load_in4(const T* p, size_t i, float out[4]);
 template <> __device__ __forceinline__ void load_in4<float>(const float* p, size_t i, float out[4]) {

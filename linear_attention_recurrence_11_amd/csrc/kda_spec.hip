@@ -93,9 +93,78 @@ void kda_spec_kernel(const InT* __restrict__ q,
         x[j] = *src;
     }
   };
+  // Commit: a block's token inputs as loaded (bf16 bits or floats): element
+  // e of this thread is i = t + e * NT of the block's nb x dk (k, g) and
+  // nb x dv (v) elements, and b is beta of token t (t < nb). Loads complete
+  // in order, so the next unit's first block is loaded right after that
+  // unit's state prefetch: loaded after the prefetch, the current unit's
+  // inputs would make their first use wait for it. (Verify has no prefetch;
+  // it stages straight from global memory, with few loads in flight, which
+  // keeps it within its register budget.)
+  constexpr int EK = (TB * DK + NT - 1) / NT, EV = (TB * DV + NT - 1) / NT;
+  struct InBlock {
+    InT q[COMMIT ? 1 : EK], k[EK], g[EK], v[EV], b;
+  };
+  auto stage_direct = [&](size_t tok0, int nb) __attribute__((always_inline)) {
+    for (int i = t; i < nb * DK; i += NT) {
+      const int j = i / DK, c = i % DK;
+      const size_t x = (tok0 + static_cast<size_t>(j) * H) * DK + c;
+      if constexpr (!COMMIT) s_q[j][c] = load_in(q, x);
+      s_k[j][c] = load_in(k, x);
+      s_e[j][c] = expf(gate_decay<GATE>(load_in(g, x)));
+    }
+    for (int i = t; i < nb * DV; i += NT) {
+      const int j = i / DV, c = i % DV;
+      s_v[j][c] = load_in(v, (tok0 + static_cast<size_t>(j) * H) * DV + c);
+    }
+    if (t < nb) s_b[t] = load_in(beta, tok0 + static_cast<size_t>(t) * H);
+  };
+  auto load_block = [&](InBlock& x, int64_t u, int64_t t0, int nb) __attribute__((always_inline)) {
+    const int64_t n = u / H, h = u % H;
+    const size_t tok0 = static_cast<size_t>((n * T + t0) * H + h);  // token j: tok0 + j * H
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int i = t + e * NT;
+      if (i < nb * DK) {
+        const size_t idx = (tok0 + static_cast<size_t>(i / DK) * H) * DK + i % DK;
+        if constexpr (!COMMIT) x.q[e] = q[idx];
+        x.k[e] = k[idx];
+        x.g[e] = g[idx];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      const int i = t + e * NT;
+      if (i < nb * DV) x.v[e] = v[(tok0 + static_cast<size_t>(i / DV) * H) * DV + i % DV];
+    }
+    if (t < nb) x.b = beta[tok0 + static_cast<size_t>(t) * H];
+  };
+  auto stage_block = [&](const InBlock& x, int nb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int i = t + e * NT;
+      if (i < nb * DK) {
+        const int j = i / DK, c = i % DK;
+        if constexpr (!COMMIT) s_q[j][c] = to_f32(x.q[e]);
+        s_k[j][c] = to_f32(x.k[e]);
+        s_e[j][c] = expf(gate_decay<GATE>(to_f32(x.g[e])));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      const int i = t + e * NT;
+      if (i < nb * DV) s_v[i / DV][i % DV] = to_f32(x.v[e]);
+    }
+    if (t < nb) s_b[t] = to_f32(x.b);
+  };
+  const int nb0 = static_cast<int>(T < TB ? T : TB);  // tokens of a first block, loaded ahead
   f32x4 next[RPT];
+  InBlock ahead{};
   int64_t unit = blockIdx.x;  // the grid never exceeds the unit count
-  if constexpr (COMMIT) load_state(unit, next);
+  if constexpr (COMMIT) {
+    load_state(unit, next);
+    load_block(ahead, unit, 0, nb0);
+  }
   for (; unit < units; unit += stride) {  // uniform per workgroup
     const int64_t n = unit / H, h = unit % H;
     float* Su = S + static_cast<size_t>(unit) * DK * DV;
@@ -103,8 +172,12 @@ void kda_spec_kernel(const InT* __restrict__ q,
     float4 s[RPT];
 #pragma unroll
     for (int j = 0; j < RPT; ++j) s[j] = make_float4(next[j][0], next[j][1], next[j][2], next[j][3]);
+    const InBlock first = ahead;
     if constexpr (COMMIT) {
-      if (unit + stride < units) load_state(unit + stride, next);
+      if (unit + stride < units) {
+        load_state(unit + stride, next);
+        load_block(ahead, unit + stride, 0, nb0);
+      }
     }
 
     int64_t ntok = T;
@@ -116,18 +189,17 @@ void kda_spec_kernel(const InT* __restrict__ q,
       const int nb = static_cast<int>(ntok - t0 < TB ? ntok - t0 : TB);
       const size_t tok0 = static_cast<size_t>((n * T + t0) * H + h);  // token j: tok0 + j * H
       __syncthreads();  // the readers of the previous block (or unit) are done
-      for (int i = t; i < nb * DK; i += NT) {
-        const int j = i / DK, c = i % DK;
-        const size_t x = (tok0 + static_cast<size_t>(j) * H) * DK + c;
-        if constexpr (!COMMIT) s_q[j][c] = load_in(q, x);
-        s_k[j][c] = load_in(k, x);
-        s_e[j][c] = expf(gate_decay<GATE>(load_in(g, x)));
+      if constexpr (COMMIT) {
+        if (t0 == 0) {
+          stage_block(first, nb);
+        } else {
+          InBlock x;
+          load_block(x, unit, t0, nb);
+          stage_block(x, nb);
+        }
+      } else {
+        stage_direct(tok0, nb);
       }
-      for (int i = t; i < nb * DV; i += NT) {
-        const int j = i / DV, c = i % DV;
-        s_v[j][c] = load_in(v, (tok0 + static_cast<size_t>(j) * H) * DV + c);
-      }
-      if (t < nb) s_b[t] = load_in(beta, tok0 + static_cast<size_t>(t) * H);
       __syncthreads();
       if constexpr (!COMMIT) {
         // q_t . k_t of each token, one wavefront per token; read after the

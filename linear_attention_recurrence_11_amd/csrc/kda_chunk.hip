@@ -316,19 +316,21 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
   uint8_t* rec = ws + static_cast<size_t>((b * H + h) * NPR + sp) * L.bytes;
 
   // ---- loads, kept packed until used: 8 consecutive channels per lane ----
+  // Every lane loads (tokens past T read token 0 of the sequence) and the
+  // padding tokens are zeroed where each value is first used: loads complete
+  // in order, and a use right after the loads (beta's conversion, or zeros
+  // written over a pending load) would wait for all of them before the
+  // channel loop starts.
+  const uint16_t braw = beta[tok];
   u32x4a8 rq[NM / 2], rk[NM / 2], rg[NM / 2];
 #pragma unroll
   for (int p = 0; p < NM / 2; ++p) {
     const size_t off = tok * DK + 32 * p + 8 * gq;
-    if (valid) {
-      rq[p] = *reinterpret_cast<const u32x4a8*>(q + off);
-      rk[p] = *reinterpret_cast<const u32x4a8*>(k + off);
-      rg[p] = *reinterpret_cast<const u32x4a8*>(g + off);
-    } else {
-      rq[p] = rk[p] = rg[p] = u32x4a8{0u, 0u, 0u, 0u};
-    }
+    rq[p] = *reinterpret_cast<const u32x4a8*>(q + off);
+    rk[p] = *reinterpret_cast<const u32x4a8*>(k + off);
+    rg[p] = *reinterpret_cast<const u32x4a8*>(g + off);
   }
-  if (gq == 0) s_beta[w][c16] = valid ? load_in(beta, tok) : 0.f;
+  const u32x4a8 kZero = {0u, 0u, 0u, 0u};
 
   // ---- per 32 channels: decay scan, scaled operands, Gram (channel
   // 32p + 8gq + i is Gram slot i of the lane) ----
@@ -336,9 +338,9 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
 #pragma unroll
   for (int p = 0; p < NM / 2; ++p) {
     float qt[8], kt[8], kh[8], xq[8], xk[8], xg[8];
-    unpack8(rq[p], xq);
-    unpack8(rk[p], xk);
-    unpack8(rg[p], xg);
+    unpack8(valid ? rq[p] : kZero, xq);
+    unpack8(valid ? rk[p] : kZero, xk);
+    unpack8(rg[p], xg);  // the decay of a padding token is zeroed below
     f16x8 kt16, kb16, qt16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -376,6 +378,7 @@ __global__ __launch_bounds__(128) void kda_chunk_prep_pair(const uint16_t* __res
     MrawT = mma_16x16x32_bf16(kh_lo, qt_hi, MrawT);
     MrawT = mma_16x16x32_bf16(kh_hi, qt_lo, MrawT);
   }
+  if (gq == 0) s_beta[w][c16] = valid ? bf16_bits_to_f32(braw) : 0.f;
   __syncthreads();  // s_beta, s_kt, s_kb, s_qt, s_eg of both chunks visible
   if (w == 0) {
     // Qt of c1 in the record's fragment order (channel 16m + 4gq + i of the

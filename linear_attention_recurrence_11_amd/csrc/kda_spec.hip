@@ -25,21 +25,24 @@
 // kCommitGrid). Thread t owns float4 column group cg = t % (dv/4) of rows
 // rg + RG*j, as in the decode step, and keeps its part of S in registers
 // across all tokens. The inputs of up to kTokBlock tokens are staged in LDS
-// at once, loaded together (in verify, while the state loads are in flight),
-// so no token waits on a global load of its own. Per token two barriers:
-// partial reductions written, u published.
+// at once (commit loads a unit's first block one unit ahead, beside that
+// unit's state), so no token waits on a global load of its own. Per token two
+// barriers: partial reductions written, u published.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-// Threads per workgroup. Verify reads the state once and has three barriers
-// per token, which favour small workgroups; commit also writes the state
-// back, which favours more wavefronts streaming it (measured on 256 requests
-// x 32 heads x 4 drafts: verify 141 us at 256 threads, 288 us at 1024;
-// commit 231 us at 256, 207 us at 1024, 200 us with the persistent grid and
-// its prefetch, which lowers verify's occupancy too far to pay there).
+// Threads per workgroup. Verify reads the state once and synchronises every
+// token, which favours small workgroups; commit also writes the state back,
+// which favours more wavefronts streaming it (measured on 256 requests x 32
+// heads x 4 drafts, with three barriers per token: verify 141 us at 256
+// threads, 288 us at 1024; commit 231 us at 256, 207 us at 1024, 200 us with
+// the persistent grid and its prefetch. Verify on that persistent grid, with
+// the current two barriers: 101 us for one draft against 130, but 212 us for
+// four against 168, its per-token reductions over 32 row groups no longer
+// hidden by other resident workgroups).
 template <bool COMMIT>
 constexpr int spec_threads() {
   return COMMIT ? 1024 : 256;

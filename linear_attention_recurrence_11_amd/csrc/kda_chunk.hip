@@ -860,6 +860,17 @@ struct Ring32Geom {
   static constexpr int kStagesRaw = 1 + 63 / (kUnitsPer + 2 * SPW);  // + the V loads
   static constexpr int kStages = kStagesRaw > 5 ? 5 : kStagesRaw;
   static_assert((kStages - 1) * (kUnitsPer + 2 * SPW) <= 63, "loads in flight exceed the wait counter");
+  // Outputs with SPW = 4: a token's 64 columns are adjacent in o, so the
+  // compute wavefronts leave each step's output tiles in LDS as rows of the
+  // pair's 32 tokens x 64 fp32, and store whole rows during the next step
+  // (one request per line instead of one per slice and line). Two buffers,
+  // by step parity. Measured: 1-7% off the pass with four slices; with two
+  // (half-line rows for bf16 outputs) it cost up to 8%, so two slices keep
+  // the direct stores.
+  static constexpr bool kMergedOut = SPW == 4;
+  static constexpr int kORow = SPW * 16 * 4;  // bytes per token row
+  static constexpr int kOPair = 32 * kORow;   // bytes per pair
+  static constexpr int kOStage = kMergedOut ? 2 * kOPair : 0;
 };
 
 // Time per 32-token step of a workgroup serving 2 or 4 slices, relative to one
@@ -938,7 +949,9 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   using G = Ring32Geom<DK, SPW>;
   constexpr int NM = DK / 16;
   constexpr int kR = G::kSlots, kS = G::kStages;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kR * G::kSlot];
+  constexpr bool kMerged = MODE == kPassOutputs && G::kMergedOut;  // outputs staged as whole rows
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kR * G::kSlot + (kMerged ? G::kOStage : 0)];
+  uint8_t* const ostage = ring + kR * G::kSlot;
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, c16 = l & 15, gq = l >> 4;
   // XCD-aware numbering, as in kda_state_pass: all slice groups of a head
@@ -1116,8 +1129,30 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_at<float>(base, lane_off + (16 * m + i) * srow, S[m][i] * up);
   };
+  // Stores the staged outputs of pair m: compute wavefront z takes tokens
+  // z * 32/SPW .. of the pair, whole rows of 16-byte pieces (64 / pieces
+  // per row tokens per instruction); tokens past T are not stored.
+  auto store_staged = [&](int64_t m) __attribute__((always_inline)) {
+    if constexpr (kMerged) {
+      constexpr int kPieces = G::kORow / 16;         // 16-byte pieces per row
+      constexpr int kTokInstr = 64 / kPieces;        // tokens per instruction
+      constexpr int kTokWave = 32 / SPW;             // tokens per wavefront
+      const uint8_t* src = ostage + static_cast<int>(m & 1) * G::kOPair;
+      OutT* om = ob + static_cast<size_t>(m) * pair_elems;
+      const int piece = l % kPieces;
+#pragma unroll
+      for (int i = 0; i < kTokWave / kTokInstr; ++i) {
+        const int tok = z * kTokWave + i * kTokInstr + l / kPieces;
+        const f32x4 x = ld_at<f32x4>(src, static_cast<uint32_t>(tok * G::kORow + piece * 16));
+        const uint32_t off = static_cast<uint32_t>(tok * H * DV + group * SPW * 16 + 4 * piece) *
+                             static_cast<uint32_t>(sizeof(OutT));
+        if (m < NPF || m * 32 + tok < T) st_out4_at(om, off, x);
+      }
+    }
+  };
   ring_barrier();
   for (int64_t n = 0; n < NPR; ++n) {
+    if (n > 0) store_staged(n - 1);  // staged last step, visible since the barrier
     PairFrags<DK> f;
     const uint8_t* slot = ring + static_cast<int>(n % kR) * G::kSlot;
     f.template load<G::kVPitch, G::kVTile>(slot, slot + G::kRec + 2 * z * G::kVTile, L, l, gq, c16);
@@ -1228,13 +1263,21 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
         O1 *= up;
         O2 *= up;
       }
-      OutT* oc = ob + static_cast<size_t>(n) * pair_elems;
-      if (n < NPF) {
-        st_out4_at(oc, obt, O1);
-        st_out4_at(oc + chunk_elems, obt, O2);
-      } else {  // last, partial pair: tokens past T are not stored
-        if (n * 32 + c16 < T) st_out4_at(oc, obt, O1);
-        if (n * 32 + 16 + c16 < T) st_out4_at(oc + chunk_elems, obt, O2);
+      if constexpr (kMerged) {
+        // this slice's columns of tokens c16 and 16 + c16; stored next step
+        uint8_t* dst = ostage + static_cast<int>(n & 1) * G::kOPair;
+        const uint32_t col = static_cast<uint32_t>(z * 64 + gq * 16);
+        st_at<f32x4>(dst, static_cast<uint32_t>(c16 * G::kORow) + col, O1);
+        st_at<f32x4>(dst, static_cast<uint32_t>((16 + c16) * G::kORow) + col, O2);
+      } else {
+        OutT* oc = ob + static_cast<size_t>(n) * pair_elems;
+        if (n < NPF) {
+          st_out4_at(oc, obt, O1);
+          st_out4_at(oc + chunk_elems, obt, O2);
+        } else {  // last, partial pair: tokens past T are not stored
+          if (n * 32 + c16 < T) st_out4_at(oc, obt, O1);
+          if (n * 32 + 16 + c16 < T) st_out4_at(oc + chunk_elems, obt, O2);
+        }
       }
     }
     if (kOut && n + 1 == next_snap && n < NPF) {
@@ -1243,6 +1286,7 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     }
     ring_barrier();
   }
+  store_staged(NPR - 1);  // the last pair, staged before the last barrier
   for (int64_t k = NPR; k < NPS; ++k) ring_barrier();  // match the loader's steps
   if constexpr (!SCALED) {
     // suspect: a non-finite entry anywhere in the slice (the sum keeps it),

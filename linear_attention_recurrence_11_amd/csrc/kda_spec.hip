@@ -19,15 +19,19 @@
 // the 64 KiB fp32 state three times (read, read, write) whatever T is, where
 // T single decode steps would move it 2T times.
 //
-// Verify runs one 256-thread workgroup per (request, head); commit runs up to
-// 1024 persistent 1024-thread workgroups that take the units in turn and
-// load the next unit's state while replaying the current one (spec_threads,
-// kCommitGrid). Thread t owns float4 column group cg = t % (dv/4) of rows
-// rg + RG*j, as in the decode step, and keeps its part of S in registers
-// across all tokens. The inputs of up to kTokBlock tokens are staged in LDS
-// at once (commit loads a unit's first block one unit ahead, beside that
-// unit's state), so no token waits on a global load of its own. Per token two
-// barriers: partial reductions written, u published.
+// Verify (kda_spec_verify_cols) gives each wavefront 16 value columns of one
+// (request, head) unit with all dk rows: every column of the state evolves on
+// its own, so the sums over rows are cross-lane exchanges and a token needs
+// no barrier. Commit (kda_spec_kernel) runs up to 1024 persistent 1024-thread
+// workgroups that take the units in turn and load the next unit's state
+// while replaying the current one (spec_threads, kCommitGrid); thread t owns
+// float4 column group cg = t % (dv/4) of rows rg + RG*j, as in the decode
+// step, with two barriers per token (partial reductions written, u
+// published). Both keep their part of S in registers across all tokens and
+// stage a block of tokens' inputs in LDS at once (commit loads a unit's
+// first block one unit ahead, beside that unit's state), so no token waits
+// on a global load of its own. Verify falls back to kda_spec_kernel (one
+// 256-thread workgroup per unit) when its inputs are not 16-byte aligned.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -268,10 +272,242 @@ void kda_spec_kernel(const InT* __restrict__ q,
   }
 }
 
+// ---- verify by column slices ---------------------------------------------
+// Every value column of the state evolves on its own: the decay scales rows,
+// and the erase and the write of column c read only column c, v_c and the
+// token's k, q and beta (the decode step's per-column form). So a wavefront
+// that holds all dk rows of 16 columns needs no other wavefront: its sums
+// over rows are cross-lane exchanges, with no LDS and no barrier per token.
+//
+// A workgroup is 4 such wavefronts, 64 columns of one (request, head) unit
+// (all of them for dv = 64). The token inputs of a block of TB tokens are
+// staged in LDS at once (q, k, e^gate and the workgroup's v columns, widened
+// to fp32), behind one barrier; the next block's inputs are loaded into
+// registers before the current block's tokens run. The loads that a staging
+// waits for are older than the previous block's output stores, but the wait
+// also covers those stores (the memory counter drains in issue order and
+// their number is not fixed), so blocks are as long as the drafts allow:
+// TB = 8 up to 8 drafts, 16 beyond (measured: 16 costs 3% at one draft, and
+// saves 9% at twelve).
+//
+// Lane l = 16 rho + 4 i + cq (rho the 16-lane row, i and cq in 0..3) holds
+// columns 4 cq .. + 3 of its wavefront's 16 in rows R rg .. + R - 1, where
+// rg = 4 rho + i and R = dk / 16. The row sums of a token are reduced and
+// scattered at once: after the exchanges, the lanes of row rho hold the sums
+// of column 4 cq + rho, where that column's u and output are formed; u then
+// returns to all four rows for the update.
+//
+// Measured at 256 requests x 32 heads, d = 128, bf16 inputs: 115, 142, 175
+// and 227 us for 1, 4, 8 and 12 drafts, against 129, 171, 216 and 262 us for
+// kda_spec_kernel. Workgroups of 8 wavefronts (a whole unit) gave 117, 149,
+// 183 and 271 us; a persistent grid loading the next unit's state ahead
+// needs about 150 registers (one workgroup per compute unit) and took 128 us
+// for one draft but 181 us for four.
+
+constexpr int kVerifyCols = 64;  // value columns per workgroup (4 wavefronts)
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+// A copy in a register of its own (identity quad permutation): the lane
+// swaps below exchange two registers, and one value passed as both operands
+// would be one register.
+__device__ __forceinline__ float own_copy(float x) { return dpp_move<0xE4>(x); }
+
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second. For a and b it returns, summed: in rows 0 and
+// 2, a over rows {0, 1} and {2, 3}; in rows 1 and 3, b over the same pairs.
+__device__ __forceinline__ float swap_add16(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(fbits(a), fbits(b), false, false);
+  return bitsf(p[0]) + bitsf(p[1]);
+}
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 of its second: summed, the low half holds a over both halves
+// and the high half b over both halves.
+__device__ __forceinline__ float swap_add32(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(fbits(a), fbits(b), false, false);
+  return bitsf(p[0]) + bitsf(p[1]);
+}
+// Sum over the four lanes 4 i + cq, i = 0..3, of each row (rotations by 8,
+// then 4: each step adds a pair of values that both of its lanes hold, so
+// the four lanes end with the same bits).
+__device__ __forceinline__ float sum_quads_of_row(float x) {
+  x += dpp_move<0x128>(x);  // row_ror:8
+  x += dpp_move<0x124>(x);  // row_ror:4
+  return x;
+}
+
+template <typename InT, typename OutT, int DK, int DV, int GATE, int TB>
+__global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda_spec_verify_cols(
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
+    const InT* __restrict__ g, const InT* __restrict__ beta, const float* __restrict__ S,
+    OutT* __restrict__ o, int64_t T, int64_t H, int64_t units) {
+  constexpr int R = DK / 16;
+  constexpr int CW = DV < kVerifyCols ? DV : kVerifyCols, NT = CW * 4, HALVES = DV / CW;
+  // a block's token inputs: 16-byte vectors of q, k, g (TB x DK each) and of
+  // this workgroup's v columns (TB x CW); thread t loads vectors t, t + NT, ...
+  constexpr int VE = 16 / sizeof(InT);
+  constexpr int NQ = TB * DK / VE, NVEC = 3 * NQ + TB * CW / VE, PER = (NVEC + NT - 1) / NT;
+  static_assert(NQ % 64 == 0 && (TB * CW / VE) % 64 == 0, "input choice uniform per wavefront");
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  struct Block {
+    u32x4v x[PER];
+    InT b;
+  };
+  __shared__ __attribute__((aligned(16))) float s_q[TB][DK], s_k[TB][DK], s_e[TB][DK], s_v[TB][CW];
+  __shared__ float s_b[TB];
+
+  // XCD-aware numbering: workgroups are dealt to the 8 XCDs in turn, so the
+  // HALVES workgroups of a unit take ids congruent mod 8 and share one L2
+  // for their common inputs
+  const int64_t bid = blockIdx.x;
+  const int64_t unit = (bid / (8 * HALVES)) * 8 + bid % 8;
+  const int half = static_cast<int>((bid / 8) % HALVES);
+  if (unit >= units) return;  // uniform per workgroup; no barrier passed yet
+  const int64_t n = unit / H, h = unit % H;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int rho = l >> 4, cq = l & 3;
+  const int row0 = R * (l >> 2), lcol = 16 * w + 4 * cq;  // first row, first local column
+  const int col = CW * half + lcol;                       // first column held
+  const int locol = lcol + rho, ocol = col + rho;         // the column formed here
+
+  // Vector i of a block is vector r of input `which` (q, k, g, v: the
+  // counts are multiples of 64, so the choice is uniform per wavefront);
+  // fn gets the input's pointer, its LDS rows, the row width in LDS, the
+  // input's row length and r.
+  auto with_vec = [&](int i, auto&& fn) __attribute__((always_inline)) {
+    if (i < NQ) fn(q, &s_q[0][0], DK, DK, i, false);
+    else if (i < 2 * NQ) fn(k, &s_k[0][0], DK, DK, i - NQ, false);
+    else if (i < 3 * NQ) fn(g, &s_e[0][0], DK, DK, i - 2 * NQ, true);
+    else if (i < NVEC) fn(v + CW * half, &s_v[0][0], CW, DV, i - 3 * NQ, false);
+  };
+  auto load_block = [&](Block& x, int64_t t0, int nb) __attribute__((always_inline)) {
+    const size_t tok0 = static_cast<size_t>((n * T + t0) * H + h);  // token j: tok0 + j * H
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      with_vec(tid + e * NT, [&](const InT* base, float*, int width, int len, int r, bool) {
+        const int j = r / (width / VE), c = (r % (width / VE)) * VE;
+        if (j < nb)
+          x.x[e] = *reinterpret_cast<const u32x4v*>(base + (tok0 + static_cast<size_t>(j) * H) * len + c);
+      });
+    }
+    if (tid < nb) x.b = beta[tok0 + static_cast<size_t>(tid) * H];
+  };
+  // Stage: widen to fp32 (g to its decay factor e^gate) into the LDS rows.
+  auto stage_block = [&](const Block& x, int nb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      with_vec(tid + e * NT, [&](const InT*, float* rows, int width, int, int r, bool decay) {
+        const int j = r / (width / VE), c = (r % (width / VE)) * VE;
+        if (j < nb) {
+          float f[VE];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            if constexpr (sizeof(InT) == 2) {  // bf16 pairs, low half first
+              f[2 * m] = __uint_as_float(x.x[e][m] << 16);
+              f[2 * m + 1] = __uint_as_float(x.x[e][m] & 0xffff0000u);
+            } else {
+              f[m] = __uint_as_float(x.x[e][m]);
+            }
+          }
+          if (decay) {
+#pragma unroll
+            for (int m = 0; m < VE; ++m) f[m] = expf(gate_decay<GATE>(f[m]));
+          }
+          float* dst = rows + j * width + c;
+#pragma unroll
+          for (int m = 0; m < VE; m += 4)
+            *reinterpret_cast<f32x4*>(dst + m) = f32x4{f[m], f[m + 1], f[m + 2], f[m + 3]};
+        }
+      });
+    }
+    if (tid < nb) s_b[tid] = to_f32(x.b);
+  };
+
+  // inputs first: loads complete in order, so staging them waits only for them
+  Block blk;
+  load_block(blk, 0, static_cast<int>(T < TB ? T : TB));
+  f32x4 s[R];
+  const float* Su = S + static_cast<size_t>(unit) * DK * DV + col;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (row0 + i) * DV));
+  for (int64_t t0 = 0; t0 < T; t0 += TB) {
+    const int nb = static_cast<int>(T - t0 < TB ? T - t0 : TB);
+    if (t0 > 0) __syncthreads();  // the readers of the previous block are done
+    stage_block(blk, nb);
+    __syncthreads();
+    if (t0 + TB < T)  // the next block's inputs, in flight while these tokens run
+      load_block(blk, t0 + TB, static_cast<int>(T - t0 - TB < TB ? T - t0 - TB : TB));
+    for (int j = 0; j < nb; ++j) {
+      float r[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+#pragma unroll
+      for (int i4 = 0; i4 < R; i4 += 4) {
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(&s_e[j][row0 + i4]);
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&s_q[j][row0 + i4]);
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&s_k[j][row0 + i4]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int i = i4 + m;
+          s[i] *= e4[m];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            r[c] += k4[m] * s[i][c];
+            p[c] += q4[m] * s[i][c];
+          }
+          qk += q4[m] * k4[m];
+        }
+      }
+      // row rho ends with S^T k and S^T q of column 4 cq + rho, every lane with qk
+      const float rs = sum_quads_of_row(swap_add32(swap_add16(r[0], r[1]), swap_add16(r[2], r[3])));
+      const float ps = sum_quads_of_row(swap_add32(swap_add16(p[0], p[1]), swap_add16(p[2], p[3])));
+      qk = swap_add16(qk, own_copy(qk));
+      qk = sum_quads_of_row(swap_add32(qk, own_copy(qk)));
+      const float u = s_b[j] * (s_v[j][locol] - rs);
+      if ((l & 12) == 0)  // one lane per column
+        store_out(o, static_cast<size_t>((n * T + t0 + j) * H + h) * DV + ocol, ps + qk * u);
+      // u of columns 4 cq + 0..3 to every row: rows {0,1} <- u0 / u1 pairs, ...
+      const auto a = __builtin_amdgcn_permlane16_swap(fbits(u), fbits(own_copy(u)), false, false);
+      const float ue = bitsf(a[0]), uo = bitsf(a[1]);  // u of rows 0, 2 / of rows 1, 3
+      const auto b = __builtin_amdgcn_permlane32_swap(fbits(ue), fbits(own_copy(ue)), false, false);
+      const auto c = __builtin_amdgcn_permlane32_swap(fbits(uo), fbits(own_copy(uo)), false, false);
+      const f32x4 uc = {bitsf(b[0]), bitsf(c[0]), bitsf(b[1]), bitsf(c[1])};
+#pragma unroll
+      for (int i4 = 0; i4 < R; i4 += 4) {  // k read again: fewer live registers
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&s_k[j][row0 + i4]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s[i4 + m] += k4[m] * uc;
+      }
+    }
+  }
+}
+
+// The column-slice verify loads its token inputs as 16-byte vectors; callers'
+// pointers need only element alignment, so other pointers take the
+// workgroup-per-unit form.
+inline bool verify_cols_aligned(const SpecArgs& a) {
+  auto ok = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return ok(a.q) && ok(a.k) && ok(a.g) && ok(a.v);
+}
+
 template <typename InT, typename OutT, int DK, int DV, int GATE, bool COMMIT>
 hipError_t launch_typed(const SpecArgs& a, hipStream_t stream) {
   const int64_t units = a.N * a.H;
-  // commit: persistent workgroups over the units; verify: one per unit
+  if constexpr (!COMMIT) {
+    constexpr int CW = DV < kVerifyCols ? DV : kVerifyCols;
+    const int64_t grid = (units + 7) / 8 * 8 * (DV / CW);  // whole groups of 8 units
+    if (verify_cols_aligned(a) && grid <= 0x7fffffff) {
+      auto kernel = a.T > 8 ? kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 16>
+                            : kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 8>;
+      hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(CW * 4), 0, stream,
+                         static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
+                         static_cast<const InT*>(a.v), static_cast<const InT*>(a.g),
+                         static_cast<const InT*>(a.beta), a.S, static_cast<OutT*>(a.o), a.T,
+                         a.H, units);
+      return hipGetLastError();
+    }
+  }
+  // commit: persistent workgroups over the units; verify (inputs not 16-byte
+  // aligned): one per unit
   const int64_t grid = COMMIT && units > kCommitGrid ? kCommitGrid : units;
   hipLaunchKernelGGL((kda_spec_kernel<InT, OutT, DK, DV, GATE, COMMIT>),
                      dim3(static_cast<uint32_t>(grid)), dim3(spec_threads<COMMIT>()), 0, stream,

@@ -176,9 +176,9 @@ def test_spec_commit_replays_the_accepted_prefix(dt):
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
 def test_spec_many_drafts_cross_token_blocks(dt, dk, dv):
-    # 19 drafts: the kernels stage the inputs of 8 tokens at a time, so this
-    # runs blocks of 8, 8 and 3; accepted counts end inside, at and next to
-    # block edges
+    # 19 drafts: commit stages the inputs of 8 tokens at a time (blocks of 8,
+    # 8 and 3), verify 16 at a time beyond 8 drafts (16 and 3); accepted
+    # counts end inside, at and next to block edges
     N, T, H = 8, 19, 2
     announce("spec many drafts", dt, dk, dv)
     ins = _spec_inputs(N, T, H, dk, dv, dt, seed=71 + dk)
@@ -200,6 +200,51 @@ def test_spec_many_drafts_cross_token_blocks(dt, dk, dv):
         one["S0"] = ins["S0"][n:n + 1]
         _, S_ref = _oracle(one)
         assert rel_err(S[n].cpu().numpy(), S_ref[0]) <= 1e-4, (n, a)
+
+
+@pytest.mark.parametrize("T", [8, 9, 16, 17, 33])
+def test_spec_verify_draft_counts_at_block_edges(T):
+    # verify stages 8 tokens per block up to 8 drafts and 16 beyond: one block
+    # exactly full, one token into a block, and three blocks; 5 x 3 units
+    # leave the last group of 8 units partly empty
+    N, H, dk, dv = 5, 3, 128, 128
+    announce("spec verify block edges", T)
+    ins = _spec_inputs(N, T, H, dk, dv, "bf16", seed=300 + T)
+    o = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"])
+    torch.cuda.synchronize()
+    o_ref, _ = _oracle(ins)
+    e = rel_err(o.cpu().numpy(), o_ref)
+    announce("err_o %.3g" % e)
+    assert e <= 1e-4
+
+
+def _shifted(x):
+    """x's values at a data pointer one element past a 16-byte boundary."""
+    flat = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+    y = flat[1:].view(x.shape)
+    y.copy_(x)
+    return y
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_spec_verify_inputs_off_16_byte_boundaries(dt):
+    # q, k, g and v only element-aligned: verify takes the workgroup-per-unit
+    # kernel (the column-slice kernel loads 16-byte vectors); both agree with
+    # the oracle and with each other
+    N, T, H, dk, dv = 4, 6, 3, 128, 128
+    announce("spec verify unaligned", dt)
+    ins = _spec_inputs(N, T, H, dk, dv, dt, seed=17)
+    o_vec = binding.kda_spec_verify(ins["q"], ins["k"], ins["v"], ins["g"], ins["beta"], ins["S0"])
+    sh = {m: _shifted(ins[m]) for m in ("q", "k", "v", "g")}
+    assert all(sh[m].data_ptr() % 16 != 0 for m in sh)
+    o_unit = binding.kda_spec_verify(sh["q"], sh["k"], sh["v"], sh["g"], ins["beta"], ins["S0"])
+    torch.cuda.synchronize()
+    o_ref, _ = _oracle(ins)
+    e_vec = rel_err(o_vec.cpu().numpy(), o_ref)
+    e_unit = rel_err(o_unit.cpu().numpy(), o_ref)
+    announce("err_o %.3g / %.3g" % (e_vec, e_unit))
+    assert e_vec <= 1e-4 and e_unit <= 1e-4
+    assert rel_err(o_vec.cpu().numpy(), o_unit.cpu().numpy().astype(np.float64)) <= 1e-5
 
 
 def test_spec_commit_more_units_than_workgroups():

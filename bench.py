@@ -361,16 +361,20 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     ev = lambda: torch.cuda.Event(enable_timing=True)
     snaps = torch.empty((B, T // every, H, dk, dv), dtype=torch.float32, device=dev)
 
-    def timed(fn):
+    def timed(fn, inner=1):
+        # `inner` calls back to back per event pair: for kernels of a few
+        # hundred microseconds the host's time in the binding would otherwise
+        # fall between the start event and the launch
         ts = []
         for r in range(reps + 1):
             a, b = ev(), ev()
             a.record(stream)
-            fn()
+            for _ in range(inner):
+                fn()
             b.record(stream)
             torch.cuda.synchronize()
             if r:
-                ts.append(a.elapsed_time(b))
+                ts.append(a.elapsed_time(b) / inner)
         return float(np.mean(ts))
 
     snap_ms = timed(lambda: binding.kda_chunk_fwd_ex(
@@ -393,12 +397,14 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     acc = torch.full((N,), accept, dtype=torch.int32, device=dev)
     Sw = d["S"].clone()
     ver_ms = timed(lambda: binding.kda_spec_verify(sp["q"], sp["k"], sp["v"], sp["g"], sp["beta"],
-                                                   Sck, o=o_sp))
-    com_ms = timed(lambda: binding.kda_spec_commit(sp["k"], sp["v"], sp["g"], sp["beta"], Sw, acc))
+                                                   Sck, o=o_sp), inner=8)
+    # each commit advances Sw by `accept` tokens: repeated commits are the same work
+    com_ms = timed(lambda: binding.kda_spec_commit(sp["k"], sp["v"], sp["g"], sp["beta"], Sw, acc),
+                   inner=8)
     o1 = torch.empty((N, Hd, dvd), dtype=torch.float32, device=dev)
     t0 = {n: sp[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta")}
     dec_ms = timed(lambda: binding.kda_decode_step(t0["q"], t0["k"], t0["v"], t0["g"], t0["beta"], Sw,
-                                                   o=o1))
+                                                   o=o1), inner=8)
     state = N * Hd * dkd * dvd * 4
     tok_in = N * Hd * (3 * dkd + dvd + 1) * 2           # q, k, g, v, beta per draft token
     ver_bytes = state + draft * (tok_in + N * Hd * dvd * 4)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -308,6 +308,49 @@ kda_status kda_spec_commit_check(const void* k, const void* v, const void* g,
                                  const void* beta, const float* S,
                                  const int32_t* accepted, int64_t N, int64_t T, int64_t H,
                                  int64_t dk, int64_t dv, int in_dtype, int gate);
+
+/*
+ * kda_spec_commit_verify: the boundary between two speculative rounds in one
+ * pass over the state (the replay of logged inputs from the checkpoint, as
+ * above). S is first advanced in place over the first accepted[n] of the T1
+ * tokens logged in the previous round (exactly as kda_spec_commit), and then
+ * o[n, t] is formed for the T2 draft tokens of the next round, stepping from
+ * the advanced state, which the drafts leave unchanged (as kda_spec_verify).
+ * The result equals kda_spec_commit followed by kda_spec_verify, up to the
+ * rounding order of the sums over dk; the state is read once and written
+ * once, where the two calls read it twice and write it once.
+ *
+ *   k1, g1    [N, T1, H, dk]  in_dtype   logged tokens of the previous round
+ *   v1        [N, T1, H, dv]  in_dtype
+ *   beta1     [N, T1, H]      in_dtype
+ *   accepted  [N] int32 on the device, 4-byte aligned; clamped to [0, T1]
+ *   q2, k2, g2 [N, T2, H, dk] in_dtype   draft tokens of the next round
+ *   v2        [N, T2, H, dv]  in_dtype
+ *   beta2     [N, T2, H]      in_dtype
+ *   S         [N, H, dk, dv] fp32, in place; 16-byte aligned
+ *   o         [N, T2, H, dv]  out_dtype
+ *
+ * S and o must not overlap any input, nor each other. T1 = 0 leaves S as it
+ * is (a plain verify); T2 = 0 writes no output (a plain commit). Pointers
+ * need element alignment only; with q2, k2, g2, v2, k1, g1 and v1 all 16-byte
+ * aligned the two steps run as one kernel, otherwise as the two calls'
+ * kernels in order. Errors as for the two calls.
+ */
+kda_status kda_spec_commit_verify(const void* k1, const void* v1, const void* g1,
+                                  const void* beta1, const int32_t* accepted, int64_t T1,
+                                  const void* q2, const void* k2, const void* v2,
+                                  const void* g2, const void* beta2, int64_t T2, float* S,
+                                  void* o, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                                  int in_dtype, int out_dtype, int gate, void* stream);
+
+/* Host-only check of kda_spec_commit_verify (see kda_chunk_fwd_check). */
+kda_status kda_spec_commit_verify_check(const void* k1, const void* v1, const void* g1,
+                                        const void* beta1, const int32_t* accepted, int64_t T1,
+                                        const void* q2, const void* k2, const void* v2,
+                                        const void* g2, const void* beta2, int64_t T2,
+                                        const float* S, const void* o, int64_t N, int64_t H,
+                                        int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                                        int gate);
 
 /*
  * Context-parallel prefill, the part one device runs: a sequence cut into

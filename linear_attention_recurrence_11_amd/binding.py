@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 # The argument lists below follow this version of include/kda.h.
-ABI_VERSION = 3
+ABI_VERSION = 4
 NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 KDA_F32, KDA_BF16 = 0, 1
 KDA_GATE_LOG_DECAY, KDA_GATE_SIGMOID = 0, 1
@@ -77,6 +77,12 @@ def _load():
         lib.kda_spec_commit.argtypes = [vp] * 6 + [i64] * 5 + [i, i, vp]
         lib.kda_spec_commit_check.restype = i
         lib.kda_spec_commit_check.argtypes = [vp] * 6 + [i64] * 5 + [i, i]
+        lib.kda_spec_commit_verify.restype = i
+        lib.kda_spec_commit_verify.argtypes = [vp] * 5 + [i64] + [vp] * 5 + [i64] + [vp] * 2 + \
+            [i64] * 4 + [i, i, i, vp]
+        lib.kda_spec_commit_verify_check.restype = i
+        lib.kda_spec_commit_verify_check.argtypes = [vp] * 5 + [i64] + [vp] * 5 + [i64] + \
+            [vp] * 2 + [i64] * 4 + [i, i, i]
         lib.kda_chunk_transition.restype = i
         lib.kda_chunk_transition.argtypes = [vp, vp, sz, vp, vp] + [i64] * 5 + [i, vp]
         lib.kda_chunk_transition_check.restype = i
@@ -407,6 +413,37 @@ def kda_spec_commit(k, v, g, beta, S, accepted, *, gate=KDA_GATE_LOG_DECAY, stre
     if st != _STATUS_OK:
         raise KDAError(st, what)
     return S
+
+
+def kda_spec_commit_verify(k1, v1, g1, beta1, accepted, q2, k2, v2, g2, beta2, S, *,
+                           gate=KDA_GATE_LOG_DECAY, o=None, out_dtype=torch.float32, stream=None):
+    """Commit of one speculative round and verify of the next in one call: S
+    [N,H,dk,dv] advanced in place over the first accepted[n] of the T1 logged
+    tokens (k1, g1 [N,T1,H,dk], v1 [N,T1,H,dv], beta1 [N,T1,H]), then the
+    outputs of the T2 drafts (q2, k2, g2 [N,T2,H,dk], v2 [N,T2,H,dv], beta2
+    [N,T2,H]) from the advanced state. Returns o [N,T2,H,dv]."""
+    what = "kda_spec_commit_verify"
+    lib = _load()
+    N, T2, H, dk = _dims(q2, 4, what, "q2")
+    dv = _dims(v2, 4, what, "v2")[-1]
+    T1 = _dims(k1, 4, what, "k1")[1]
+    dt = _in_dtypes(q2)
+    dev = _check(what, [("k1", k1, (N, T1, H, dk), dt, True), ("v1", v1, (N, T1, H, dv), dt, True),
+                        ("g1", g1, (N, T1, H, dk), dt, True), ("beta1", beta1, (N, T1, H), dt, True),
+                        ("accepted", accepted, (N,), (torch.int32,), True),
+                        ("q2", q2, (N, T2, H, dk), dt, True), ("k2", k2, (N, T2, H, dk), dt, True),
+                        ("v2", v2, (N, T2, H, dv), dt, True), ("g2", g2, (N, T2, H, dk), dt, True),
+                        ("beta2", beta2, (N, T2, H), dt, True), ("S", S, (N, H, dk, dv), _F32, True),
+                        ("o", o, (N, T2, H, dv), _OUT, False)])
+    if o is None:
+        o = torch.empty((N, T2, H, dv), dtype=out_dtype, device=dev)
+    st = lib.kda_spec_commit_verify(_ptr(k1), _ptr(v1), _ptr(g1), _ptr(beta1), _ptr(accepted), T1,
+                                    _ptr(q2), _ptr(k2), _ptr(v2), _ptr(g2), _ptr(beta2), T2,
+                                    _ptr(S), _ptr(o), N, H, dk, dv, _dcode(q2.dtype),
+                                    _dcode(o.dtype), int(gate), _stream(stream, dev))
+    if st != _STATUS_OK:
+        raise KDAError(st, what)
+    return o
 
 
 def kda_chunk_transition(workspace, B, T, H, dk, dv, in_dtype, *, v=None, F=None, E=None,

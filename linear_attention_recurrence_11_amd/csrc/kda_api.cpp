@@ -392,6 +392,59 @@ kda_status kda_spec_commit(const void* k, const void* v, const void* g, const vo
   return launch_status(kda::launch_spec(a, true, static_cast<hipStream_t>(stream)));
 }
 
+
+kda_status kda_spec_commit_verify_check(const void* k1, const void* v1, const void* g1,
+                                        const void* beta1, const int32_t* accepted, int64_t T1,
+                                        const void* q2, const void* k2, const void* v2,
+                                        const void* g2, const void* beta2, int64_t T2,
+                                        const float* S, const void* o, int64_t N, int64_t H,
+                                        int64_t dk, int64_t dv, int in_dtype, int out_dtype,
+                                        int gate) {
+  // each step's own rules, then those across the two token sets: S is
+  // written (after the logged tokens are read) and must not overlap the
+  // drafts; o must not overlap the logged tokens or the accepted counts
+  kda_status st = check_spec(true, nullptr, k1, v1, g1, beta1, S, nullptr, accepted, N, T1, H, dk,
+                             dv, in_dtype, KDA_F32, gate);
+  if (st != KDA_OK) return st;
+  st = check_spec(false, q2, k2, v2, g2, beta2, S, o, nullptr, N, T2, H, dk, dv, in_dtype,
+                  out_dtype, gate);
+  if (st != KDA_OK) return st;
+  const int64_t NH = N * H;
+  if (NH == 0 || T1 == 0 || T2 == 0) return KDA_OK;
+  const int64_t es = dsize(in_dtype), eo = dsize(out_dtype);
+  const Range rs = range_of(S, NH * dk * dv, 4);
+  const Range ro = range_of(o, N * T2 * H * dv, eo);
+  const Range drafts[] = {range_of(q2, N * T2 * H * dk, es), range_of(k2, N * T2 * H * dk, es),
+                          range_of(v2, N * T2 * H * dv, es), range_of(g2, N * T2 * H * dk, es),
+                          range_of(beta2, N * T2 * H, es)};
+  for (const Range& x : drafts)
+    if (overlap(rs, x)) return KDA_ERR_ALIAS;
+  const Range logged[] = {range_of(k1, N * T1 * H * dk, es), range_of(v1, N * T1 * H * dv, es),
+                          range_of(g1, N * T1 * H * dk, es), range_of(beta1, N * T1 * H, es),
+                          range_of(accepted, N, 4)};
+  for (const Range& x : logged)
+    if (overlap(ro, x)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status kda_spec_commit_verify(const void* k1, const void* v1, const void* g1,
+                                  const void* beta1, const int32_t* accepted, int64_t T1,
+                                  const void* q2, const void* k2, const void* v2,
+                                  const void* g2, const void* beta2, int64_t T2, float* S,
+                                  void* o, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                                  int in_dtype, int out_dtype, int gate, void* stream) {
+  const kda_status st =
+      kda_spec_commit_verify_check(k1, v1, g1, beta1, accepted, T1, q2, k2, v2, g2, beta2, T2, S,
+                                   o, N, H, dk, dv, in_dtype, out_dtype, gate);
+  if (st != KDA_OK) return st;
+  if (N * H == 0 || (T1 == 0 && T2 == 0)) return KDA_OK;
+  kda::SpecArgs a{q2, k2, v2, g2, beta2, S, o, nullptr, N, T2, H, dk, dv, in_dtype, out_dtype};
+  a.gate = gate;
+  const kda::SpecPrefix pre{k1, v1, g1, beta1, accepted, T1};
+  if (injected_failure()) return KDA_ERR_HIP;
+  return launch_status(kda::launch_spec_commit_verify(a, pre, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace {

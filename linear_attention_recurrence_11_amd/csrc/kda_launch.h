@@ -140,4 +140,15 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t stream);
 // Launch a speculative verification (commit = false) or commit (commit = true).
 hipError_t launch_spec(const SpecArgs& a, bool commit, hipStream_t stream);
 
+// The previous round's logged tokens for kda_spec_commit_verify: k1, g1
+// [N, T1, H, dk], v1 [N, T1, H, dv], beta1 [N, T1, H] and the accepted
+// counts; the SpecArgs beside them describe the next round's drafts.
+struct SpecPrefix {
+  const void *k1, *v1, *g1, *beta1;
+  const int32_t* accepted;
+  int64_t T1;
+};
+hipError_t launch_spec_commit_verify(const SpecArgs& drafts, const SpecPrefix& pre,
+                                     hipStream_t stream);
+
 }  // namespace kda

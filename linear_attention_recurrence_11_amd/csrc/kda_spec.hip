@@ -336,11 +336,19 @@ __device__ __forceinline__ float sum_quads_of_row(float x) {
   return x;
 }
 
-template <typename InT, typename OutT, int DK, int DV, int GATE, int TB>
+// FUSED: the same kernel first replays the accepted prefix of the previous
+// round's logged tokens (k1, v1, g1, beta1; accepted[n] of T1, as in the
+// commit), writes the advanced state back once, and then verifies the drafts
+// from it (commit followed by verify, with one read and one write of the
+// state instead of two reads and one write). Blocks hold tokens of one set:
+// the prefix's first, then the drafts'.
+template <typename InT, typename OutT, int DK, int DV, int GATE, int TB, bool FUSED>
 __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda_spec_verify_cols(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
-    const InT* __restrict__ g, const InT* __restrict__ beta, const float* __restrict__ S,
-    OutT* __restrict__ o, int64_t T, int64_t H, int64_t units) {
+    const InT* __restrict__ g, const InT* __restrict__ beta, float* __restrict__ S,
+    OutT* __restrict__ o, int64_t T, int64_t H, int64_t units, const InT* __restrict__ k1,
+    const InT* __restrict__ v1, const InT* __restrict__ g1, const InT* __restrict__ beta1,
+    const int32_t* __restrict__ accepted, int64_t T1) {
   constexpr int R = DK / 16;
   constexpr int CW = DV < kVerifyCols ? DV : kVerifyCols, NT = CW * 4, HALVES = DV / CW;
   // a block's token inputs: 16-byte vectors of q, k, g (TB x DK each) and of
@@ -370,35 +378,64 @@ __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda
   const int col = CW * half + lcol;                       // first column held
   const int locol = lcol + rho, ocol = col + rho;         // the column formed here
 
-  // Vector i of a block is vector r of input `which` (q, k, g, v: the
-  // counts are multiples of 64, so the choice is uniform per wavefront);
-  // fn gets the input's pointer, its LDS rows, the row width in LDS, the
-  // input's row length and r.
-  auto with_vec = [&](int i, auto&& fn) __attribute__((always_inline)) {
-    if (i < NQ) fn(q, &s_q[0][0], DK, DK, i, false);
-    else if (i < 2 * NQ) fn(k, &s_k[0][0], DK, DK, i - NQ, false);
-    else if (i < 3 * NQ) fn(g, &s_e[0][0], DK, DK, i - 2 * NQ, true);
-    else if (i < NVEC) fn(v + CW * half, &s_v[0][0], CW, DV, i - 3 * NQ, false);
+  // Tokens: ntok of the prefix (FUSED), then the T drafts; block b holds
+  // prefix tokens [b TB, ..) for b < nc, else drafts [(b - nc) TB, ..).
+  int64_t ntok = 0;
+  if constexpr (FUSED) {
+    const int64_t acc = accepted[n];
+    ntok = acc < 0 ? 0 : (acc > T1 ? T1 : acc);
+  }
+  const int64_t nc = (ntok + TB - 1) / TB, nblocks = nc + (T + TB - 1) / TB;
+  if (nblocks == 0) return;  // uniform per workgroup
+  struct Where {
+    bool pre;  // a block of the prefix
+    int64_t t0;
+    int nb;
   };
-  auto load_block = [&](Block& x, int64_t t0, int nb) __attribute__((always_inline)) {
-    const size_t tok0 = static_cast<size_t>((n * T + t0) * H + h);  // token j: tok0 + j * H
+  auto where = [&](int64_t b) {
+    Where x;
+    x.pre = FUSED && b < nc;
+    x.t0 = (x.pre ? b : b - nc) * TB;
+    const int64_t left = (x.pre ? ntok : T) - x.t0;
+    x.nb = static_cast<int>(left < TB ? left : TB);
+    return x;
+  };
+
+  // Vector i of a block is vector r of input `which` (q, k, g, v: the
+  // counts are multiples of 64, so the choice is uniform per wavefront; the
+  // prefix has no q); fn gets the input's pointer, its LDS rows, the row
+  // width in LDS, the input's row length and r.
+  auto with_vec = [&](int i, bool pre, auto&& fn) __attribute__((always_inline)) {
+    if (i < NQ) {
+      if (!pre) fn(q, &s_q[0][0], DK, DK, i, false);
+    } else if (i < 2 * NQ) {
+      fn(pre ? k1 : k, &s_k[0][0], DK, DK, i - NQ, false);
+    } else if (i < 3 * NQ) {
+      fn(pre ? g1 : g, &s_e[0][0], DK, DK, i - 2 * NQ, true);
+    } else if (i < NVEC) {
+      fn((pre ? v1 : v) + CW * half, &s_v[0][0], CW, DV, i - 3 * NQ, false);
+    }
+  };
+  auto load_block = [&](Block& x, const Where& wb) __attribute__((always_inline)) {
+    const int64_t tn = wb.pre ? T1 : T;  // tokens per request in that set
+    const size_t tok0 = static_cast<size_t>((n * tn + wb.t0) * H + h);  // token j: tok0 + j * H
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      with_vec(tid + e * NT, [&](const InT* base, float*, int width, int len, int r, bool) {
+      with_vec(tid + e * NT, wb.pre, [&](const InT* base, float*, int width, int len, int r, bool) {
         const int j = r / (width / VE), c = (r % (width / VE)) * VE;
-        if (j < nb)
+        if (j < wb.nb)
           x.x[e] = *reinterpret_cast<const u32x4v*>(base + (tok0 + static_cast<size_t>(j) * H) * len + c);
       });
     }
-    if (tid < nb) x.b = beta[tok0 + static_cast<size_t>(tid) * H];
+    if (tid < wb.nb) x.b = (wb.pre ? beta1 : beta)[tok0 + static_cast<size_t>(tid) * H];
   };
   // Stage: widen to fp32 (g to its decay factor e^gate) into the LDS rows.
-  auto stage_block = [&](const Block& x, int nb) __attribute__((always_inline)) {
+  auto stage_block = [&](const Block& x, const Where& wb) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      with_vec(tid + e * NT, [&](const InT*, float* rows, int width, int, int r, bool decay) {
+      with_vec(tid + e * NT, wb.pre, [&](const InT*, float* rows, int width, int, int r, bool decay) {
         const int j = r / (width / VE), c = (r % (width / VE)) * VE;
-        if (j < nb) {
+        if (j < wb.nb) {
           float f[VE];
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
@@ -420,31 +457,40 @@ __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda
         }
       });
     }
-    if (tid < nb) s_b[tid] = to_f32(x.b);
+    if (tid < wb.nb) s_b[tid] = to_f32(x.b);
   };
 
   // inputs first: loads complete in order, so staging them waits only for them
   Block blk;
-  load_block(blk, 0, static_cast<int>(T < TB ? T : TB));
+  load_block(blk, where(0));
+  float* const Su = S + static_cast<size_t>(unit) * DK * DV + col;
   f32x4 s[R];
-  const float* Su = S + static_cast<size_t>(unit) * DK * DV + col;
 #pragma unroll
   for (int i = 0; i < R; ++i)
     s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (row0 + i) * DV));
-  for (int64_t t0 = 0; t0 < T; t0 += TB) {
-    const int nb = static_cast<int>(T - t0 < TB ? T - t0 : TB);
-    if (t0 > 0) __syncthreads();  // the readers of the previous block are done
-    stage_block(blk, nb);
+  for (int64_t b = 0; b < nblocks; ++b) {
+    const Where wb = where(b);
+    if (b > 0) __syncthreads();  // the readers of the previous block are done
+    stage_block(blk, wb);
     __syncthreads();
-    if (t0 + TB < T)  // the next block's inputs, in flight while these tokens run
-      load_block(blk, t0 + TB, static_cast<int>(T - t0 - TB < TB ? T - t0 - TB : TB));
-    for (int j = 0; j < nb; ++j) {
+    if (b + 1 < nblocks) load_block(blk, where(b + 1));  // in flight while these tokens run
+    if (FUSED && nc > 0 && b == nc) {
+      // the accepted prefix is in: the new checkpoint, stored once the first
+      // drafts are staged (stores issued earlier would hold up that wait,
+      // which drains in issue order)
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (row0 + i) * DV));
+    }
+    for (int j = 0; j < wb.nb; ++j) {
+      // decay, then S^T k (and for a draft S^T q and q . k) of the lane's rows
       float r[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
 #pragma unroll
       for (int i4 = 0; i4 < R; i4 += 4) {
         const f32x4 e4 = *reinterpret_cast<const f32x4*>(&s_e[j][row0 + i4]);
-        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&s_q[j][row0 + i4]);
         const f32x4 k4 = *reinterpret_cast<const f32x4*>(&s_k[j][row0 + i4]);
+        f32x4 q4 = zero4();
+        if (!wb.pre) q4 = *reinterpret_cast<const f32x4*>(&s_q[j][row0 + i4]);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int i = i4 + m;
@@ -457,20 +503,22 @@ __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda
           qk += q4[m] * k4[m];
         }
       }
-      // row rho ends with S^T k and S^T q of column 4 cq + rho, every lane with qk
+      // row rho ends with the sums of column 4 cq + rho
       const float rs = sum_quads_of_row(swap_add32(swap_add16(r[0], r[1]), swap_add16(r[2], r[3])));
-      const float ps = sum_quads_of_row(swap_add32(swap_add16(p[0], p[1]), swap_add16(p[2], p[3])));
-      qk = swap_add16(qk, own_copy(qk));
-      qk = sum_quads_of_row(swap_add32(qk, own_copy(qk)));
       const float u = s_b[j] * (s_v[j][locol] - rs);
-      if ((l & 12) == 0)  // one lane per column
-        store_out(o, static_cast<size_t>((n * T + t0 + j) * H + h) * DV + ocol, ps + qk * u);
+      if (!wb.pre) {  // a draft: its output, from the state before its write
+        const float ps = sum_quads_of_row(swap_add32(swap_add16(p[0], p[1]), swap_add16(p[2], p[3])));
+        qk = swap_add16(qk, own_copy(qk));
+        qk = sum_quads_of_row(swap_add32(qk, own_copy(qk)));
+        if ((l & 12) == 0)  // one lane per column
+          store_out(o, static_cast<size_t>((n * T + wb.t0 + j) * H + h) * DV + ocol, ps + qk * u);
+      }
       // u of columns 4 cq + 0..3 to every row: rows {0,1} <- u0 / u1 pairs, ...
       const auto a = __builtin_amdgcn_permlane16_swap(fbits(u), fbits(own_copy(u)), false, false);
       const float ue = bitsf(a[0]), uo = bitsf(a[1]);  // u of rows 0, 2 / of rows 1, 3
-      const auto b = __builtin_amdgcn_permlane32_swap(fbits(ue), fbits(own_copy(ue)), false, false);
-      const auto c = __builtin_amdgcn_permlane32_swap(fbits(uo), fbits(own_copy(uo)), false, false);
-      const f32x4 uc = {bitsf(b[0]), bitsf(c[0]), bitsf(b[1]), bitsf(c[1])};
+      const auto bb = __builtin_amdgcn_permlane32_swap(fbits(ue), fbits(own_copy(ue)), false, false);
+      const auto cc = __builtin_amdgcn_permlane32_swap(fbits(uo), fbits(own_copy(uo)), false, false);
+      const f32x4 uc = {bitsf(bb[0]), bitsf(cc[0]), bitsf(bb[1]), bitsf(cc[1])};
 #pragma unroll
       for (int i4 = 0; i4 < R; i4 += 4) {  // k read again: fewer live registers
         const f32x4 k4 = *reinterpret_cast<const f32x4*>(&s_k[j][row0 + i4]);
@@ -481,72 +529,131 @@ __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda
   }
 }
 
-// The column-slice verify loads its token inputs as 16-byte vectors; callers'
-// pointers need only element alignment, so other pointers take the
-// workgroup-per-unit form.
+// The column-slice kernel loads token inputs as 16-byte vectors; callers'
+// pointers need only element alignment, so verify with other pointers takes
+// the workgroup-per-unit form, and the fused call the two separate calls.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 inline bool verify_cols_aligned(const SpecArgs& a) {
-  auto ok = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  return ok(a.q) && ok(a.k) && ok(a.g) && ok(a.v);
+  return aligned16(a.q) && aligned16(a.k) && aligned16(a.g) && aligned16(a.v);
 }
 
-template <typename InT, typename OutT, int DK, int DV, int GATE, bool COMMIT>
-hipError_t launch_typed(const SpecArgs& a, hipStream_t stream) {
+enum SpecMode { kSpecVerify = 0, kSpecCommit = 1, kSpecFused = 2 };
+
+// The column-slice kernel over whole groups of 8 units; false if the grid
+// would exceed the launch limit (the caller then takes another form).
+template <typename InT, typename OutT, int DK, int DV, int GATE, bool FUSED>
+bool launch_cols(const SpecArgs& a, const SpecPrefix* pre, hipStream_t stream, hipError_t* err) {
+  constexpr int CW = DV < kVerifyCols ? DV : kVerifyCols;
   const int64_t units = a.N * a.H;
-  if constexpr (!COMMIT) {
-    constexpr int CW = DV < kVerifyCols ? DV : kVerifyCols;
-    const int64_t grid = (units + 7) / 8 * 8 * (DV / CW);  // whole groups of 8 units
-    if (verify_cols_aligned(a) && grid <= 0x7fffffff) {
-      auto kernel = a.T > 8 ? kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 16>
-                            : kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 8>;
-      hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(CW * 4), 0, stream,
-                         static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
-                         static_cast<const InT*>(a.v), static_cast<const InT*>(a.g),
-                         static_cast<const InT*>(a.beta), a.S, static_cast<OutT*>(a.o), a.T,
-                         a.H, units);
-      return hipGetLastError();
-    }
-  }
-  // commit: persistent workgroups over the units; verify (inputs not 16-byte
-  // aligned): one per unit
-  const int64_t grid = COMMIT && units > kCommitGrid ? kCommitGrid : units;
-  hipLaunchKernelGGL((kda_spec_kernel<InT, OutT, DK, DV, GATE, COMMIT>),
-                     dim3(static_cast<uint32_t>(grid)), dim3(spec_threads<COMMIT>()), 0, stream,
+  const int64_t grid = (units + 7) / 8 * 8 * (DV / CW);
+  if (grid > 0x7fffffff) return false;
+  const int64_t tmax = FUSED && pre->T1 > a.T ? pre->T1 : a.T;
+  auto kernel = tmax > 8 ? kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 16, FUSED>
+                         : kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 8, FUSED>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(CW * 4), 0, stream,
                      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
                      static_cast<const InT*>(a.v), static_cast<const InT*>(a.g),
-                     static_cast<const InT*>(a.beta), a.S, static_cast<OutT*>(a.o), a.accepted,
-                     a.T, a.H, units);
-  return hipGetLastError();
+                     static_cast<const InT*>(a.beta), a.S, static_cast<OutT*>(a.o), a.T, a.H,
+                     units, static_cast<const InT*>(FUSED ? pre->k1 : nullptr),
+                     static_cast<const InT*>(FUSED ? pre->v1 : nullptr),
+                     static_cast<const InT*>(FUSED ? pre->g1 : nullptr),
+                     static_cast<const InT*>(FUSED ? pre->beta1 : nullptr),
+                     FUSED ? pre->accepted : nullptr, FUSED ? pre->T1 : int64_t{0});
+  *err = hipGetLastError();
+  return true;
 }
 
-template <typename InT, typename OutT, int DK, int DV, bool COMMIT>
-hipError_t launch_gate(const SpecArgs& a, hipStream_t s) {
-  return a.gate == kGateSigmoid ? launch_typed<InT, OutT, DK, DV, kGateSigmoid, COMMIT>(a, s)
-                                : launch_typed<InT, OutT, DK, DV, kGateLogDecay, COMMIT>(a, s);
+template <typename InT, typename OutT, int DK, int DV, int GATE, int MODE>
+hipError_t launch_typed(const SpecArgs& a, const SpecPrefix* pre, hipStream_t stream) {
+  const int64_t units = a.N * a.H;
+  hipError_t err = hipSuccess;
+  if constexpr (MODE == kSpecFused) {
+    if (verify_cols_aligned(a) && aligned16(pre->k1) && aligned16(pre->g1) && aligned16(pre->v1) &&
+        launch_cols<InT, OutT, DK, DV, GATE, true>(a, pre, stream, &err))
+      return err;
+    // element-aligned inputs: the commit, then the verify
+    SpecArgs c = a;
+    c.q = nullptr;
+    c.k = pre->k1;
+    c.v = pre->v1;
+    c.g = pre->g1;
+    c.beta = pre->beta1;
+    c.o = nullptr;
+    c.accepted = pre->accepted;
+    c.T = pre->T1;
+    err = launch_typed<InT, float, DK, DV, GATE, kSpecCommit>(c, nullptr, stream);
+    if (err != hipSuccess) return err;
+    return launch_typed<InT, OutT, DK, DV, GATE, kSpecVerify>(a, nullptr, stream);
+  } else {
+    constexpr bool COMMIT = MODE == kSpecCommit;
+    if (!COMMIT && verify_cols_aligned(a) &&
+        launch_cols<InT, OutT, DK, DV, GATE, false>(a, nullptr, stream, &err))
+      return err;
+    // commit: persistent workgroups over the units; verify (inputs not 16-byte
+    // aligned): one per unit
+    const int64_t grid = COMMIT && units > kCommitGrid ? kCommitGrid : units;
+    hipLaunchKernelGGL((kda_spec_kernel<InT, OutT, DK, DV, GATE, COMMIT>),
+                       dim3(static_cast<uint32_t>(grid)), dim3(spec_threads<COMMIT>()), 0, stream,
+                       static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
+                       static_cast<const InT*>(a.v), static_cast<const InT*>(a.g),
+                       static_cast<const InT*>(a.beta), a.S, static_cast<OutT*>(a.o), a.accepted,
+                       a.T, a.H, units);
+    return hipGetLastError();
+  }
 }
 
-template <typename InT, typename OutT, bool COMMIT>
-hipError_t launch_shape(const SpecArgs& a, hipStream_t s) {
+template <typename InT, typename OutT, int DK, int DV, int MODE>
+hipError_t launch_gate(const SpecArgs& a, const SpecPrefix* pre, hipStream_t s) {
+  return a.gate == kGateSigmoid ? launch_typed<InT, OutT, DK, DV, kGateSigmoid, MODE>(a, pre, s)
+                                : launch_typed<InT, OutT, DK, DV, kGateLogDecay, MODE>(a, pre, s);
+}
+
+template <typename InT, typename OutT, int MODE>
+hipError_t launch_shape(const SpecArgs& a, const SpecPrefix* pre, hipStream_t s) {
   if (a.dk == 64)
-    return a.dv == 64 ? launch_gate<InT, OutT, 64, 64, COMMIT>(a, s)
-                      : launch_gate<InT, OutT, 64, 128, COMMIT>(a, s);
-  return a.dv == 64 ? launch_gate<InT, OutT, 128, 64, COMMIT>(a, s)
-                    : launch_gate<InT, OutT, 128, 128, COMMIT>(a, s);
+    return a.dv == 64 ? launch_gate<InT, OutT, 64, 64, MODE>(a, pre, s)
+                      : launch_gate<InT, OutT, 64, 128, MODE>(a, pre, s);
+  return a.dv == 64 ? launch_gate<InT, OutT, 128, 64, MODE>(a, pre, s)
+                    : launch_gate<InT, OutT, 128, 128, MODE>(a, pre, s);
+}
+
+template <int MODE>
+hipError_t launch_out(const SpecArgs& a, const SpecPrefix* pre, hipStream_t stream) {
+  const bool in32 = a.in_dtype == 0, out32 = a.out_dtype == 0;
+  if (in32)
+    return out32 ? launch_shape<float, float, MODE>(a, pre, stream)
+                 : launch_shape<float, uint16_t, MODE>(a, pre, stream);
+  return out32 ? launch_shape<uint16_t, float, MODE>(a, pre, stream)
+               : launch_shape<uint16_t, uint16_t, MODE>(a, pre, stream);
 }
 
 }  // namespace
 
 hipError_t launch_spec(const SpecArgs& a, bool commit, hipStream_t stream) {
   if (a.N * a.H == 0 || a.T == 0) return hipSuccess;
-  const bool in32 = a.in_dtype == 0;
   if (commit)  // no output: the output type is immaterial
-    return in32 ? launch_shape<float, float, true>(a, stream)
-                : launch_shape<uint16_t, float, true>(a, stream);
-  const bool out32 = a.out_dtype == 0;
-  if (in32)
-    return out32 ? launch_shape<float, float, false>(a, stream)
-                 : launch_shape<float, uint16_t, false>(a, stream);
-  return out32 ? launch_shape<uint16_t, float, false>(a, stream)
-               : launch_shape<uint16_t, uint16_t, false>(a, stream);
+    return a.in_dtype == 0 ? launch_shape<float, float, kSpecCommit>(a, nullptr, stream)
+                           : launch_shape<uint16_t, float, kSpecCommit>(a, nullptr, stream);
+  return launch_out<kSpecVerify>(a, nullptr, stream);
+}
+
+hipError_t launch_spec_commit_verify(const SpecArgs& drafts, const SpecPrefix& pre,
+                                     hipStream_t stream) {
+  if (drafts.N * drafts.H == 0) return hipSuccess;
+  if (pre.T1 == 0) return launch_spec(drafts, false, stream);
+  if (drafts.T == 0) {  // the commit alone
+    SpecArgs c = drafts;
+    c.q = nullptr;
+    c.k = pre.k1;
+    c.v = pre.v1;
+    c.g = pre.g1;
+    c.beta = pre.beta1;
+    c.o = nullptr;
+    c.accepted = pre.accepted;
+    c.T = pre.T1;
+    return launch_spec(c, true, stream);
+  }
+  return launch_out<kSpecFused>(drafts, &pre, stream);
 }
 
 }  // namespace kda

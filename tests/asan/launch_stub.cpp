@@ -19,6 +19,9 @@ hipError_t launch_affine_scan(const float*, const float*, const float*, float*, 
 }
 hipError_t launch_decode_step(const DecodeArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_spec(const SpecArgs&, bool, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_spec_commit_verify(const SpecArgs&, const SpecPrefix&, hipStream_t) {
+  return hipErrorNoDevice;
+}
 hipError_t noalloc_scratch(void**) { return hipErrorNoDevice; }
 
 }  // namespace kda

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert binding.kda_abi_version() == binding.ABI_VERSION == 3
+    assert binding.kda_abi_version() == binding.ABI_VERSION == 4
     for s in range(9):
         assert binding.kda_status_str(s) and binding.kda_status_str(s) != "unknown status"
     assert binding.kda_status_str(99) == "unknown status"
@@ -285,6 +285,42 @@ def test_spec_checks(lib):
     st = lib.kda_spec_commit(*[vp(x) for x in a[1:5]], vp(a[5]), vp(a[5]), N, T, H, dk, dv, BF16, 0,
                              None)
     assert st == ALIAS
+
+
+def test_spec_commit_verify_checks(lib):
+    # the fused round boundary: each step's rules, and across the two token
+    # sets S (written) off the drafts and o off the logged tokens
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None
+    N, H, dk, dv = 3, 2, 128, 64
+    names = ["k1", "v1", "g1", "beta1", "acc", "q2", "k2", "v2", "g2", "beta2", "S", "o"]
+    base = {n: BASE + i * (1 << 24) for i, n in enumerate(names)}
+
+    def cv(T1=4, T2=5, gate=0, **over):
+        p = dict(base, **over)
+        return lib.kda_spec_commit_verify_check(
+            *[vp(p[n]) for n in names[:5]], T1, *[vp(p[n]) for n in names[5:10]], T2,
+            vp(p["S"]), vp(p["o"]), N, H, dk, dv, BF16, F32, gate)
+
+    assert cv() == OK and cv(gate=1) == OK
+    assert cv(gate=3) == UNSUP
+    assert cv(acc=None) == NULL                      # the commit needs accepted
+    assert cv(q2=None) == NULL                       # the verify reads q
+    assert cv(T1=0, k1=None, v1=None, g1=None, beta1=None, acc=None) == OK   # a plain verify
+    assert cv(T2=0, q2=None, k2=None, v2=None, g2=None, beta2=None, o=None) == OK  # a plain commit
+    assert cv(T1=0, T2=0, **{n: None for n in names}) == OK
+    assert cv(S=base["v1"]) == ALIAS                 # S over a logged input
+    assert cv(S=base["k2"]) == ALIAS                 # S over a draft
+    assert cv(o=base["S"]) == ALIAS                  # o over the state
+    assert cv(o=base["g1"]) == ALIAS                 # o over a logged input
+    assert cv(o=base["acc"]) == ALIAS                # o over the accepted counts
+    assert cv(o=base["v2"]) == ALIAS                 # o over a draft
+    assert cv(S=base["S"] + 8) == ALIGN              # the state: 16 bytes
+    assert cv(acc=base["acc"] + 2) == ALIGN          # accepted: 4 bytes
+    assert cv(k2=base["k2"] + 2) == OK               # inputs: element alignment only
+    st = lib.kda_spec_commit_verify(*[vp(base[n]) for n in names[:5]], 4,
+                                    *[vp(base[n]) for n in names[5:10]], 5, vp(base["S"]),
+                                    vp(base["S"]), N, H, dk, dv, BF16, F32, 0, None)
+    assert st == ALIAS                               # checked before any launch
 
 
 def test_transition_and_scan_checks(lib):

@@ -247,6 +247,103 @@ def test_spec_verify_inputs_off_16_byte_boundaries(dt):
     assert rel_err(o_vec.cpu().numpy(), o_unit.cpu().numpy().astype(np.float64)) <= 1e-5
 
 
+def _round_inputs(N, T1, T2, H, dk, dv, dt, seed):
+    pre = _spec_inputs(N, T1, H, dk, dv, dt, seed=seed)
+    drafts = _spec_inputs(N, T2, H, dk, dv, dt, seed=seed + 1)
+    return pre, drafts
+
+
+def _commit_verify_oracle(pre, drafts, acc_list):
+    """S after each request's accepted prefix of the logged tokens, then the
+    drafts' outputs from it (fp64 oracle)."""
+    S_out, o_out = [], []
+    for n, a in enumerate(acc_list):
+        a = max(0, min(a, pre["k"].shape[1]))
+        S_n = pre["S0"][n:n + 1].cpu()
+        if a > 0:
+            one = {m: pre[m][n:n + 1, :a].contiguous() for m in ("q", "k", "v", "g", "beta")}
+            one["S0"] = S_n
+            _, S_a = _oracle(one)
+            S_n = torch.from_numpy(np.ascontiguousarray(S_a, dtype=np.float32))
+        S_out.append(S_n.numpy().astype(np.float64))
+        d = {m: drafts[m][n:n + 1].contiguous() for m in ("q", "k", "v", "g", "beta")}
+        d["S0"] = S_n
+        o_n, _ = _oracle(d)
+        o_out.append(o_n)
+    return np.concatenate(S_out), np.concatenate(o_out)
+
+
+def _separate(pre, drafts, accepted):
+    S = pre["S0"].clone()
+    binding.kda_spec_commit(pre["k"], pre["v"], pre["g"], pre["beta"], S, accepted)
+    o = binding.kda_spec_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"], drafts["beta"], S)
+    return S, o
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+@pytest.mark.parametrize("T1,T2,acc_list", [(5, 4, [0, 1, 5, 7, -2, 3]),
+                                           (19, 11, [0, 8, 16, 17, 19, 3])],
+                         ids=["short", "blocks_of_16"])
+def test_spec_commit_verify_matches_commit_then_verify(dt, dk, dv, T1, T2, acc_list):
+    # one pass: the previous round's accepted prefix (clamped counts
+    # included), the new checkpoint, and the next round's drafts from it;
+    # the second case crosses blocks of 16 tokens in both sets
+    N, H = len(acc_list), 3
+    announce("spec commit+verify", dt, dk, dv, T1, T2)
+    pre, drafts = _round_inputs(N, T1, T2, H, dk, dv, dt, seed=500 + dk + dv + T1)
+    accepted = torch.tensor(acc_list, dtype=torch.int32, device=DEV)
+    S = pre["S0"].clone()
+    o = binding.kda_spec_commit_verify(pre["k"], pre["v"], pre["g"], pre["beta"], accepted,
+                                       drafts["q"], drafts["k"], drafts["v"], drafts["g"],
+                                       drafts["beta"], S)
+    S_sep, o_sep = _separate(pre, drafts, accepted)
+    torch.cuda.synchronize()
+    S_ref, o_ref = _commit_verify_oracle(pre, drafts, acc_list)
+    e_S, e_o = rel_err(S.cpu().numpy(), S_ref), rel_err(o.cpu().numpy(), o_ref)
+    announce("err S %.3g o %.3g" % (e_S, e_o))
+    assert e_S <= 1e-4 and e_o <= 1e-4
+    for n, a in enumerate(acc_list):
+        if a <= 0:  # nothing accepted: the checkpoint is untouched
+            assert torch.equal(S[n], pre["S0"][n])
+    # the two separate calls (other reduction orders): to fp32 rounding
+    assert rel_err(S.cpu().numpy(), S_sep.cpu().numpy().astype(np.float64)) <= 1e-5
+    assert rel_err(o.cpu().numpy(), o_sep.cpu().numpy().astype(np.float64)) <= 1e-5
+
+
+def test_spec_commit_verify_degenerate_rounds_and_unaligned_inputs():
+    # T1 = 0 is the verify, T2 = 0 the commit, and element-aligned inputs run
+    # the two calls' kernels: each bit-identical to the separate calls
+    N, H, dk, dv = 4, 3, 128, 128
+    announce("spec commit+verify degenerate")
+    pre, drafts = _round_inputs(N, 6, 4, H, dk, dv, "bf16", seed=640)
+    accepted = torch.tensor([2, 0, 6, 4], dtype=torch.int32, device=DEV)
+    S_sep, o_sep = _separate(pre, drafts, accepted)
+    empty = {m: pre[m][:, :0] for m in ("k", "v", "g", "beta")}
+    S = pre["S0"].clone()
+    o = binding.kda_spec_commit_verify(empty["k"], empty["v"], empty["g"], empty["beta"], accepted,
+                                       drafts["q"], drafts["k"], drafts["v"], drafts["g"],
+                                       drafts["beta"], S)
+    o_ver = binding.kda_spec_verify(drafts["q"], drafts["k"], drafts["v"], drafts["g"],
+                                    drafts["beta"], pre["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(S, pre["S0"]) and torch.equal(o, o_ver)
+    S = pre["S0"].clone()
+    none = {m: drafts[m][:, :0] for m in ("q", "k", "v", "g", "beta")}
+    o = binding.kda_spec_commit_verify(pre["k"], pre["v"], pre["g"], pre["beta"], accepted,
+                                       none["q"], none["k"], none["v"], none["g"], none["beta"], S)
+    torch.cuda.synchronize()
+    assert o.shape == (N, 0, H, dv) and torch.equal(S, S_sep)
+    sh1 = dict(pre, **{m: _shifted(pre[m]) for m in ("k", "v", "g")})
+    sh2 = dict(drafts, **{m: _shifted(drafts[m]) for m in ("q", "k", "v", "g")})
+    S_sep, o_sep = _separate(sh1, sh2, accepted)  # the verify's workgroup-per-unit form
+    S = pre["S0"].clone()
+    o = binding.kda_spec_commit_verify(sh1["k"], sh1["v"], sh1["g"], sh1["beta"], accepted,
+                                       sh2["q"], sh2["k"], sh2["v"], sh2["g"], sh2["beta"], S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_sep) and torch.equal(o, o_sep)
+
+
 def test_spec_commit_more_units_than_workgroups():
     # 41 x 26 = 1066 units against at most 1024 persistent workgroups, with
     # a different accepted count per request (zero included): the prefetch

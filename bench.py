@@ -356,7 +356,8 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     the prefill with bf16 output, the prefill with a state snapshot every
     `every` tokens (prefix reuse), speculative verify of `draft` tokens +
     commit of `accept` of them for the decode batch against the decode steps
-    they replace, and the prefill computed span by span through the
+    they replace (and that commit fused with the next round's verify), and
+    the prefill computed span by span through the
     context-split entry points (one GPU)."""
     ev = lambda: torch.cuda.Event(enable_timing=True)
     snaps = torch.empty((B, T // every, H, dk, dv), dtype=torch.float32, device=dev)
@@ -401,6 +402,14 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
     # each commit advances Sw by `accept` tokens: repeated commits are the same work
     com_ms = timed(lambda: binding.kda_spec_commit(sp["k"], sp["v"], sp["g"], sp["beta"], Sw, acc),
                    inner=8)
+    # the next round's drafts after this one: its commit and their verify in
+    # one call (each call replays the same accepted prefix onto Sf)
+    sp2 = inputs.make_forward(N, draft, Hd, dkd, dvd, "bf16", s0="zero", seed=4322, device=dev)
+    Sf = d["S"].clone()
+    fused_ms = timed(lambda: binding.kda_spec_commit_verify(
+        sp["k"], sp["v"], sp["g"], sp["beta"], acc, sp2["q"], sp2["k"], sp2["v"], sp2["g"],
+        sp2["beta"], Sf, o=o_sp), inner=8)
+    del sp2, Sf
     o1 = torch.empty((N, Hd, dvd), dtype=torch.float32, device=dev)
     t0 = {n: sp[n][:, 0].contiguous() for n in ("q", "k", "v", "g", "beta")}
     dec_ms = timed(lambda: binding.kda_decode_step(t0["q"], t0["k"], t0["v"], t0["g"], t0["beta"], Sw,
@@ -425,6 +434,9 @@ def measure_next(binding, inputs, ins, ws, o, ST, d, B, T, H, dk, dv, stream, de
                  "verify_GBps": round(ver_bytes / (ver_ms * 1e-3) / 1e9, 1),
                  "commit_us": round(com_ms * 1e3, 2),
                  "commit_GBps": round(com_bytes / (com_ms * 1e-3) / 1e9, 1),
+                 "commit_then_verify_next_fused_us": round(fused_ms * 1e3, 2),
+                 "fused_GBps": round((com_bytes + ver_bytes - state) / (fused_ms * 1e-3) / 1e9, 1),
+                 "fused_vs_separate": round(fused_ms / (ver_ms + com_ms), 4),
                  "decode_step_us": round(dec_ms * 1e3, 2),
                  "verify_plus_commit_vs_decode_steps": round((ver_ms + com_ms) / (draft * dec_ms), 4)},
     }

@@ -528,6 +528,11 @@ __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda
       }
     }
   }
+  if (FUSED && nc > 0 && nblocks == nc) {  // no drafts (the launcher sends that case to the commit)
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(Su + (row0 + i) * DV));
+  }
 }
 
 // The column-slice kernel loads token inputs as 16-byte vectors; callers'

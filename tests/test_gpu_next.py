@@ -344,6 +344,54 @@ def test_spec_commit_verify_degenerate_rounds_and_unaligned_inputs():
     assert torch.equal(S, S_sep) and torch.equal(o, o_sep)
 
 
+def test_spec_full_batch_sampled_units():
+    # the benchmark's batch (256 requests x 32 heads, 8,192 units, 16,384
+    # column-slice workgroups): verify, commit and the fused commit + next
+    # verify (bf16 output) on one batch, each checked on sampled units
+    N, H, dk, dv, T = 256, 32, 128, 128, 4
+    announce("spec full batch")
+    pre, drafts = _round_inputs(N, T, T, H, dk, dv, "bf16", seed=777)
+    gen = torch.Generator().manual_seed(778)
+    acc_list = torch.randint(0, T + 1, (N,), generator=gen).tolist()
+    accepted = torch.tensor(acc_list, dtype=torch.int32, device=DEV)
+    o_ver = binding.kda_spec_verify(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], pre["S0"])
+    S_com = pre["S0"].clone()
+    binding.kda_spec_commit(pre["k"], pre["v"], pre["g"], pre["beta"], S_com, accepted)
+    S_fus = pre["S0"].clone()
+    o_fus = binding.kda_spec_commit_verify(pre["k"], pre["v"], pre["g"], pre["beta"], accepted,
+                                           drafts["q"], drafts["k"], drafts["v"], drafts["g"],
+                                           drafts["beta"], S_fus, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(S_com, S_fus) or rel_err(S_fus.cpu().numpy(), S_com.cpu().numpy().astype(np.float64)) <= 1e-5
+    picks = [(0, 0), (N - 1, H - 1), (37, 5), (128, 31), (200, 16), (255, 0), (9, 9), (64, 24)]
+    worst = 0.0
+    for n, h in picks:
+        unit = lambda x, t=None: x[n:n + 1, :, h:h + 1].contiguous()
+        one = {m: unit(pre[m]) for m in ("q", "k", "v", "g", "beta")}
+        one["S0"] = pre["S0"][n:n + 1, h:h + 1]
+        o_ref, _ = _oracle(one)
+        e1 = rel_err(o_ver[n:n + 1, :, h:h + 1].cpu().numpy(), o_ref)
+        d1 = {m: unit(drafts[m]) for m in ("q", "k", "v", "g", "beta")}
+        a = acc_list[n]
+        if a > 0:
+            pa = {m: one[m][:, :a].contiguous() for m in ("q", "k", "v", "g", "beta")}
+            pa["S0"] = one["S0"]
+            _, S_a = _oracle(pa)
+        else:
+            S_a = one["S0"].cpu().numpy().astype(np.float64)
+        e2 = rel_err(S_fus[n:n + 1, h:h + 1].cpu().numpy(), S_a)
+        d1["S0"] = torch.from_numpy(np.ascontiguousarray(S_a, dtype=np.float32))
+        o2_ref, _ = _oracle(d1)
+        x3 = o_fus[n:n + 1, :, h:h + 1].float().cpu().numpy().astype(np.float64)
+        worst = max(worst, e1, e2)
+        assert e1 <= 1e-4 and e2 <= 1e-4, (n, h, e1, e2)
+        # bf16 output: each element rounded to 2^-9 of itself (bar 2^-8), on
+        # top of the fp32 path's 1e-4 of the rms
+        bar = 2.0 ** -8 * np.abs(o2_ref) + 1e-4 * np.sqrt(np.mean(o2_ref ** 2))
+        assert np.all(np.abs(x3 - o2_ref) <= bar), (n, h, float(np.max(np.abs(x3 - o2_ref) - bar)))
+    announce("worst %.3g" % worst)
+
+
 def test_spec_commit_more_units_than_workgroups():
     # 41 x 26 = 1066 units against at most 1024 persistent workgroups, with
     # a different accepted count per request (zero included): the prefetch

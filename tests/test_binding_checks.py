@@ -126,3 +126,19 @@ def test_decode_and_speculative_checks():
            sp["beta"], d["S"], acc[:2].contiguous())
     expect(ValueError, "k is on cpu", binding.kda_spec_commit, sp["k"], sp["v"], sp["g"],
            sp["beta"], d["S"], acc)
+    # the fused commit + next verify: the logged set takes its sizes from k1,
+    # the drafts from q2 (a different token count), and both share N, H, dk, dv
+    T2 = 2
+    dr = dict(q=z(N, T2, H, 128), k=z(N, T2, H, 128), v=z(N, T2, H, 64), g=z(N, T2, H, 128),
+              beta=z(N, T2, H))
+    fused = lambda **o: binding.kda_spec_commit_verify(
+        *(o.get(n, sp[n[:-1]]) for n in ("k1", "v1", "g1", "beta1")), o.get("acc", acc),
+        *(o.get(n, dr[n[:-1]]) for n in ("q2", "k2", "v2", "g2", "beta2")), o.get("S", d["S"]),
+        **({"o": o["o"]} if "o" in o else {}))
+    expect(ValueError, "v1 has shape", fused, v1=sp["v"][:, :2].contiguous())
+    expect(ValueError, "k2 has shape", fused, k2=sp["k"])
+    expect(ValueError, "beta2 has dtype", fused, beta2=dr["beta"].float())
+    expect(ValueError, "accepted has shape", fused, acc=acc[:3].contiguous())
+    expect(ValueError, "S has dtype", fused, S=d["S"].to(torch.bfloat16))
+    expect(ValueError, "o has shape", fused, o=torch.zeros(N, Td, H, 64))
+    expect(ValueError, "k1 is on cpu", fused)

@@ -343,7 +343,7 @@ __device__ __forceinline__ float sum_quads_of_row(float x) {
 // from it (commit followed by verify, with one read and one write of the
 // state instead of two reads and one write). Blocks hold tokens of one set:
 // the prefix's first, then the drafts'.
-template <typename InT, typename OutT, int DK, int DV, int GATE, int TB, bool FUSED>
+template <typename InT, typename OutT, int DK, int DV, int GATE, int TB, bool FUSED, bool STREAM>
 __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda_spec_verify_cols(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ g, const InT* __restrict__ beta, float* __restrict__ S,
@@ -464,11 +464,21 @@ __global__ __launch_bounds__((DV < kVerifyCols ? DV : kVerifyCols) * 4) void kda
   // inputs first: loads complete in order, so staging them waits only for them
   Block blk;
   load_block(blk, where(0));
+  // The state: a 128-byte line holds 32 columns, which two wavefronts read
+  // half each. Plain loads keep the line in the L2 for the second half;
+  // loads with the streaming hint fetched about a quarter of the lines twice
+  // (counters: 1.24x the algorithmic bytes), yet were faster for one or two
+  // drafts (STREAM, chosen by the launcher).
   float* const Su = S + static_cast<size_t>(unit) * DK * DV + col;
   f32x4 s[R];
+  if constexpr (STREAM) {
 #pragma unroll
-  for (int i = 0; i < R; ++i)
-    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (row0 + i) * DV));
+    for (int i = 0; i < R; ++i)
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Su + (row0 + i) * DV));
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i) s[i] = *reinterpret_cast<const f32x4*>(Su + (row0 + i) * DV);
+  }
   for (int64_t b = 0; b < nblocks; ++b) {
     const Where wb = where(b);
     if (b > 0) __syncthreads();  // the readers of the previous block are done
@@ -553,9 +563,13 @@ bool launch_cols(const SpecArgs& a, const SpecPrefix* pre, hipStream_t stream, h
   const int64_t units = a.N * a.H;
   const int64_t grid = (units + 7) / 8 * 8 * (DV / CW);
   if (grid > 0x7fffffff) return false;
+  // blocks of 16 tokens beyond 8 in either set; streaming state loads only
+  // for a plain verify of one or two drafts (measured: 112 against 125 us at
+  // one draft; plain loads are faster from four drafts on, and always fused)
   const int64_t tmax = FUSED && pre->T1 > a.T ? pre->T1 : a.T;
-  auto kernel = tmax > 8 ? kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 16, FUSED>
-                         : kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 8, FUSED>;
+  auto kernel = tmax > 8  ? kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 16, FUSED, false>
+                : FUSED || a.T > 2 ? kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 8, FUSED, false>
+                                   : kda_spec_verify_cols<InT, OutT, DK, DV, GATE, 8, FUSED, !FUSED>;
   hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(CW * 4), 0, stream,
                      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k),
                      static_cast<const InT*>(a.v), static_cast<const InT*>(a.g),

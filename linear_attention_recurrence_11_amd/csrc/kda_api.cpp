@@ -65,7 +65,7 @@ size_t kda_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
   const double total = static_cast<double>(B) * H * units * bytes;
   if (total > 9.0e18) return 0;
   if (units == 0 || B * H == 0) return 0;
-  const int64_t cols = dk > dv ? dk : dv;  // the transition's passes run over dk columns
+  const int64_t cols = dk + dv;  // the transition's F and E run as one pass over dk + dv columns
   const int64_t flags = in_dtype == KDA_F32 ? 0 : (B * H * (cols / 16) * 4 + 1023) / 1024 * 1024;
   return static_cast<size_t>(B * H * units * bytes + flags);
 }

@@ -58,8 +58,9 @@ constexpr bool kIsF32 = std::is_same<InT, float>::value;
 // kPassState, only the final state; kPassTransition, the state transition of
 // the tokens (each 16-column slice starts from its columns of the dk x dk
 // identity with v = 0, so S_T is the matrix F with S_out = F S_in + the
-// state reached from S_in = 0). The last two write no outputs.
-constexpr int kPassOutputs = 0, kPassState = 1, kPassTransition = 2;
+// state reached from S_in = 0); kPassFE, F and that state E in one pass over
+// dk + dv columns (bf16 inputs). The last three write no outputs.
+constexpr int kPassOutputs = 0, kPassState = 1, kPassTransition = 2, kPassFE = 3;
 
 // Four fp32 values as bf16 [high parts | low parts]: x = hi + lo to about 16
 // bits. A 16-deep contraction against an exact bf16 operand repeated in both
@@ -944,7 +945,7 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     const uint16_t* __restrict__ v, const uint8_t* __restrict__ ws, const float* S0,
     OutT* __restrict__ o, float* ST, float* __restrict__ snap, int64_t snap_pairs, int64_t T,
     int64_t H, int64_t DV, int64_t NPR, int64_t ngroups, int64_t nheads, PairLayout L,
-    int* __restrict__ flags) {
+    int* __restrict__ flags, float* __restrict__ E_out) {
   static_assert(!SCALED || SPW == 1, "the scaled pass serves one slice per workgroup");
   using G = Ring32Geom<DK, SPW>;
   constexpr int NM = DK / 16;
@@ -966,8 +967,11 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   }
   const int64_t b = head / H, h = head % H;
   const uint8_t* rec0 = ws + static_cast<size_t>(head) * NPR * G::kRec;
-  const size_t hb = static_cast<size_t>(b * T * H + h) * DV;
-  const size_t pair_elems = static_cast<size_t>(32 * H) * DV;  // v or o elements per 32 tokens
+  // kPassFE: the slices run over dk + dv columns, F's dk first, then E's dv;
+  // v (and o) rows hold DVV = dv values
+  const int64_t DVV = MODE == kPassFE ? DV - DK : DV;
+  const size_t hb = static_cast<size_t>(b * T * H + h) * DVV;
+  const size_t pair_elems = static_cast<size_t>(32 * H) * DVV;  // v or o elements per 32 tokens
   const int64_t NPF = T / 32;                                  // full pairs
   const int64_t NPS = (NPR + kS - 1) / kS * kS;                // loader steps (and barriers)
 
@@ -986,7 +990,21 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     // 4cq + 3 of each slice of the group
     const int va = l & 15, cq = l >> 4;
     const uint32_t vcol = static_cast<uint32_t>(group * SPW * 16 + 4 * cq);
-    const uint32_t vrow = static_cast<uint32_t>(H * DV);  // elements per token
+    const uint32_t vrow = static_cast<uint32_t>(H * DVV);  // elements per token
+    // kPassFE: slice s < dk / 16 is a column block of F (v = 0: its loads
+    // read column 0 and are zeroed at commit), the others of E at column
+    // (s - dk / 16) * 16
+    auto vcol_of = [&](int z) __attribute__((always_inline)) -> uint32_t {
+      if constexpr (MODE == kPassFE) {
+        const int sl = static_cast<int>(group) * SPW + z;
+        return static_cast<uint32_t>(sl >= DK / 16 ? (sl - DK / 16) * 16 + 4 * cq : 4 * cq);
+      } else {
+        return vcol + 16u * static_cast<uint32_t>(z);
+      }
+    };
+    auto v_on = [&](int z) __attribute__((always_inline)) {
+      return MODE != kPassFE || static_cast<int>(group) * SPW + z >= DK / 16;
+    };
     const uint16_t* vb = v + hb;
     // Loads are unconditional (pairs past the end re-read the last one; V
     // tokens past T read the last token and are zeroed at commit): a branch
@@ -1006,8 +1024,8 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
         const uint16_t* vp = vb + static_cast<size_t>(cc) * pair_elems;
 #pragma unroll
         for (int z = 0; z < SPW; ++z) {
-          st.v0[z] = ld_at<u32x2>(vp, (t0 * vrow + vcol + 16 * z) * 2u);
-          st.v1[z] = ld_at<u32x2>(vp, (t1 * vrow + vcol + 16 * z) * 2u);
+          st.v0[z] = ld_at<u32x2>(vp, (t0 * vrow + vcol_of(z)) * 2u);
+          st.v1[z] = ld_at<u32x2>(vp, (t1 * vrow + vcol_of(z)) * 2u);
         }
         st.ok0 = c * 32 + 2 * va < T;
         st.ok1 = c * 32 + 2 * va + 1 < T;
@@ -1031,8 +1049,9 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
 #pragma unroll
         for (int z = 0; z < SPW; ++z) {
           uint8_t* vt = dst + G::kRec + (2 * z + (va >> 3)) * G::kVTile + (va & 7) * 4;
-          const uint32_t r0[2] = {st.ok0 ? st.v0[z][0] : 0u, st.ok0 ? st.v0[z][1] : 0u};
-          const uint32_t r1[2] = {st.ok1 ? st.v1[z][0] : 0u, st.ok1 ? st.v1[z][1] : 0u};
+          const bool k0 = st.ok0 && v_on(z), k1 = st.ok1 && v_on(z);
+          const uint32_t r0[2] = {k0 ? st.v0[z][0] : 0u, k0 ? st.v0[z][1] : 0u};
+          const uint32_t r1[2] = {k1 ? st.v1[z][0] : 0u, k1 ? st.v1[z][1] : 0u};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const uint32_t b0 = (c & 1) ? (r0[c >> 1] >> 16) : (r0[c >> 1] & 0xffffu);
@@ -1083,7 +1102,9 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
   }
   // the slice in [dk, DV] row-major fp32 at a uniform base: per-lane byte
   // offsets of rows 4gq + i of channel group 0 (DK * DV * 4 < 2^32)
-  const uint32_t srow = static_cast<uint32_t>(DV) * 4u;
+  // kPassFE: F's slices (slice < dk / 16) are dk wide, E's dv wide
+  const bool fe_f = MODE == kPassFE && slice < DK / 16;
+  const uint32_t srow = static_cast<uint32_t>(MODE == kPassFE ? (fe_f ? DK : DVV) : DV) * 4u;
   const uint32_t slane = static_cast<uint32_t>(4 * gq) * srow + static_cast<uint32_t>(c16) * 4u;
 
   // The state and update products take fp16 operands, so the state S and
@@ -1112,6 +1133,8 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     for (int i = 0; i < 4; ++i) {
       if constexpr (MODE == kPassTransition)
         S[m][i] = (16 * m + 4 * gq + i == col) ? 1.f : 0.f;
+      else if constexpr (MODE == kPassFE)  // F from the identity, E from zero
+        S[m][i] = (fe_f && 16 * m + 4 * gq + i == col) ? 1.f : 0.f;
       else
         S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
     }
@@ -1307,7 +1330,14 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     if (l == 0) flags[head * (DV / 16) + slice] = suspect ? 1 : 0;
     if (suspect) return;
   }
-  if (ST) store_slice(ST + static_cast<size_t>(head) * DK * DV + slice * 16);
+  if constexpr (MODE == kPassFE) {
+    if (fe_f)
+      store_slice(ST + static_cast<size_t>(head) * DK * DK + slice * 16);
+    else
+      store_slice(E_out + static_cast<size_t>(head) * DK * DVV + (slice - DK / 16) * 16);
+  } else {
+    if (ST) store_slice(ST + static_cast<size_t>(head) * DK * DV + slice * 16);
+  }
 }
 
 // T = 0: the final state is the initial one (or zeros).
@@ -1368,7 +1398,7 @@ hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t 
                      dim3(static_cast<uint32_t>(blocks)), dim3(64 * (G::kLoaders + SPW)), 0, stream,
                      static_cast<const uint16_t*>(a.v), static_cast<const uint8_t*>(a.workspace),
                      a.S0, static_cast<OutT*>(a.o), a.S_T, snap_pairs > 0 ? a.snapshots : nullptr,
-                     snap_pairs, a.T, a.H, a.dv, NPR, ngroups, nheads, P, flags);
+                     snap_pairs, a.T, a.H, a.dv, NPR, ngroups, nheads, P, flags, a.E_out);
   return hipGetLastError();
 }
 
@@ -1417,7 +1447,7 @@ hipError_t launch_pass_typed(const ChunkFwdArgs& a, hipStream_t stream) {
       MODE == kPassOutputs && wants_snapshots(a) ? a.snapshot_every / 16 : 0;
   if constexpr (!kIsF32<InT>) {  // bf16 inputs: 32 tokens per step
     const int64_t snap_pairs = snap_chunks / 2;
-    if constexpr (MODE != kPassOutputs) {
+    if constexpr (MODE != kPassOutputs && MODE != kPassFE) {
       return launch_ring32_pair<OutT, DK, 1, MODE>(a, 0, stream);
     } else {
       int dev = 0, cus = 256;
@@ -1503,6 +1533,15 @@ hipError_t launch_chunk_transition(const ChunkFwdArgs& a, float* F, float* E, hi
   t.o = nullptr;
   t.snapshots = nullptr;
   t.snapshot_every = 0;
+  if (F && E && !in32) {
+    // both in one pass over dk + dv columns: [F | E] is one state, from
+    // [I | 0] with v taken as [0 | v] (each column evolves on its own), so
+    // the slices of F and E share the record stream of their head
+    t.dv = a.dk + a.dv;
+    t.S_T = F;
+    t.E_out = E;
+    return launch_pass_dk<uint16_t, float, kPassFE>(t, stream);
+  }
   if (F) {  // dk columns from the identity, v = 0
     t.dv = a.dk;
     t.S_T = F;

@@ -85,6 +85,7 @@ struct ChunkFwdArgs {
   int gate = kGateLogDecay;
   float* snapshots = nullptr;     // [B, T / snapshot_every, H, dk, dv] or null
   int64_t snapshot_every = 0;     // tokens between snapshots, a multiple of 32
+  float* E_out = nullptr;         // the transition's E beside F (one pass over dk + dv columns)
 };
 
 struct DecodeArgs {

@@ -46,12 +46,13 @@ def test_version_and_status_strings(lib):
 def test_workspace_size(lib):
     # fp32 inputs: one record per (b, h, 16-token chunk), whole KiB: 27648 B
     # (dk 128), 15360 B (dk 64); bf16 inputs: one per (b, h, pair of chunks):
-    # 30720 B (dk 128), 18432 B (dk 64), then a 4-byte flag per (b, h, 16-column
-    # slice), rounded up to whole KiB
+    # 30720 B (dk 128), 18432 B (dk 64), then a 4-byte flag per (b, h, 16
+    # columns of dk + dv: the transition's F and E run as one pass), rounded up
+    # to whole KiB
     assert binding.kda_chunk_fwd_workspace_size(1, 65536, 32, 128, 128, BF16) == \
-        32 * 2048 * 30720 + 1024
+        32 * 2048 * 30720 + 2048
     assert binding.kda_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, BF16) == \
-        64 * 128 * 30720 + 2048
+        64 * 128 * 30720 + 4096
     assert binding.kda_chunk_fwd_workspace_size(1, 33, 2, 64, 64, BF16) == 2 * 2 * 18432 + 1024
     assert binding.kda_chunk_fwd_workspace_size(1, 256, 2, 64, 64, F32) == 2 * 16 * 15360
     assert binding.kda_chunk_fwd_workspace_size(1, 17, 1, 128, 128, F32) == 2 * 27648
@@ -345,9 +346,9 @@ def test_transition_and_scan_checks(lib):
     assert tr(dk=96) == UNSUP
     assert tr(T=-1) == SHAPE
     assert tr(T=0, ws=None, ws_bytes=0, v=None) == OK
-    # the workspace also holds one flag per 16 columns of the wider of dk, dv
+    # the workspace also holds one flag per 16 columns of dk + dv
     assert binding.kda_chunk_fwd_workspace_size(1, 32, 64, 128, 16, BF16) == \
-        64 * 30720 + (64 * 8 * 4 + 1023) // 1024 * 1024
+        64 * 30720 + (64 * 9 * 4 + 1023) // 1024 * 1024
     sc = lambda P=3, N=4, dk=128, dv=64, **o: lib.kda_state_affine_scan_check(
         vp(o.get("F", F)), vp(o.get("E", E)), vp(o.get("S0", BASE)), vp(o.get("S", BASE + (1 << 38))),
         P, N, dk, dv)

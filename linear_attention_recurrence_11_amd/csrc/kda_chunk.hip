@@ -874,6 +874,23 @@ struct Ring32Geom {
   static constexpr int kOStage = kMergedOut ? 2 * kOPair : 0;
 };
 
+// Outputs on a wavefront of their own (plain pass, output mode, one slice per
+// workgroup, dk = 128). With one slice per compute unit the compute wavefront
+// is the pass's critical path: it is busy about 92% of each step, the loaders
+// 68-81% (shader-clock totals per wavefront, 64K-token workload). The output
+// products (11 of the step's 30 MFMAs) and the output stores need the state
+// only through its fp16 operand and [U1; U2], so the compute wavefront leaves
+// those in LDS (two buffers by step parity) and an output wavefront forms and
+// stores pair n's outputs during step n + 1, from the Q~ and M fragments it
+// read from pair n's slot during step n.
+template <int DK, int SPW, int MODE, bool SCALED>
+struct Ring32Split {
+  static constexpr bool kOn = DK == 128 && SPW == 1 && MODE == kPassOutputs && !SCALED;
+  static constexpr int kXPair = (DK / 32 + 1) * 1024;  // fp16 state operand + [U1; U2] fragments
+  static constexpr int kXStage = kOn ? 2 * kXPair : 0;
+  static constexpr int kWaves = Ring32Geom<DK, SPW>::kLoaders + SPW + (kOn ? 1 : 0);
+};
+
 // Time per 32-token step of a workgroup serving 2 or 4 slices, relative to one
 // slice per workgroup (measured with 32 heads of 128 x 128 over 64K tokens,
 // one workgroup per compute unit: 1.47, 1.65 and 2.04 ms).
@@ -941,18 +958,21 @@ struct PairFrags {
 // MODE (kPassOutputs, kPassState or kPassTransition): the transition loads
 // no V; the two state-only modes skip the output products and stores.
 template <typename OutT, int DK, int SPW, bool SCALED, int MODE>
-__global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kda_state_pass_ring32(
+__global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) void kda_state_pass_ring32(
     const uint16_t* __restrict__ v, const uint8_t* __restrict__ ws, const float* S0,
     OutT* __restrict__ o, float* ST, float* __restrict__ snap, int64_t snap_pairs, int64_t T,
     int64_t H, int64_t DV, int64_t NPR, int64_t ngroups, int64_t nheads, PairLayout L,
     int* __restrict__ flags, float* __restrict__ E_out) {
   static_assert(!SCALED || SPW == 1, "the scaled pass serves one slice per workgroup");
   using G = Ring32Geom<DK, SPW>;
+  using X = Ring32Split<DK, SPW, MODE, SCALED>;
   constexpr int NM = DK / 16;
   constexpr int kR = G::kSlots, kS = G::kStages;
   constexpr bool kMerged = MODE == kPassOutputs && G::kMergedOut;  // outputs staged as whole rows
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kR * G::kSlot + (kMerged ? G::kOStage : 0)];
+  constexpr int kOStageBytes = kMerged ? G::kOStage : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kR * G::kSlot + kOStageBytes + X::kXStage];
   uint8_t* const ostage = ring + kR * G::kSlot;
+  uint8_t* const xbuf = ostage + kOStageBytes;  // compute -> output wavefront (X::kOn)
 
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, c16 = l & 15, gq = l >> 4;
   // XCD-aware numbering, as in kda_state_pass: all slice groups of a head
@@ -1084,6 +1104,62 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     return;
   }
 
+  if constexpr (X::kOn) {
+    if (wave == kLd + SPW) {
+      // ---------------- outputs (one slice per workgroup) ----------------
+      // Step n reads the Q~ and M fragments of pair n from its slot (the
+      // compute wavefront reads the same slot in the same step) and forms the
+      // outputs of pair n - 1 from the fragments read in step n - 1 and the
+      // compute wavefront's fp16 state operand and [U1; U2] of pair n - 1, in
+      // the same product order as the compute wavefront's own output form.
+      OutT* obo = o + hb;
+      const uint32_t oto = static_cast<uint32_t>(c16 * H * DV + group * 16 + 4 * gq) *
+                           static_cast<uint32_t>(sizeof(OutT));
+      const size_t half = pair_elems / 2;
+      PairFrags<DK> prev;
+      ring_barrier();
+      for (int64_t n = 0; n <= NPR; ++n) {
+        PairFrags<DK> cur;
+        if (n < NPR) {
+          const uint8_t* slot = ring + static_cast<int>(n % kR) * G::kSlot;
+          cur.template load<G::kVPitch, G::kVTile>(slot, slot + G::kRec, L, l, gq, c16);
+        }
+        if (n > 0) {
+          const int64_t m = n - 1;
+          const uint8_t* xb = xbuf + static_cast<int>(m & 1) * X::kXPair;
+          f16x8 sh[NM / 2];
+#pragma unroll
+          for (int p = 0; p < NM / 2; ++p) sh[p] = ld_at<f16x8>(xb, static_cast<uint32_t>(p * 64 + l) * 16);
+          const f16x8 u12 = ld_at<f16x8>(xb, static_cast<uint32_t>((NM / 2) * 64 + l) * 16);
+          f16x8 u11;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) u11[i] = u11[i + 4] = u12[i];
+          f32x4 O1 = zero4(), O2 = zero4();
+#pragma unroll
+          for (int p = 0; p < NM / 2; ++p) {
+            O1 = mma_16x16x32_f16(sh[p], prev.q1[p], O1);
+            O2 = mma_16x16x32_f16(sh[p], prev.q2[p], O2);
+          }
+          O1 = mma_16x16x32_f16(u11, prev.m1, O1);
+          O2 = mma_16x16x32_f16(u12, prev.m2h, O2);
+          O2 = mma_16x16x32_f16(u12, prev.m2l, O2);
+          OutT* oc = obo + static_cast<size_t>(m) * pair_elems;
+          if (m < NPF) {
+            st_out4_at(oc, oto, O1);
+            st_out4_at(oc + half, oto, O2);
+          } else {  // last, partial pair: tokens past T are not stored
+            if (m * 32 + c16 < T) st_out4_at(oc, oto, O1);
+            if (m * 32 + 16 + c16 < T) st_out4_at(oc + half, oto, O2);
+          }
+        }
+        prev = cur;
+        if (n < NPR) ring_barrier();
+      }
+      for (int64_t k = NPR; k < NPS; ++k) ring_barrier();  // match the loader's steps
+      return;
+    }
+  }
+
   // ---------------- compute ----------------
   const int z = wave - kLd;  // this wavefront's slice within the group
   const int64_t slice = group * SPW + z;
@@ -1139,6 +1215,7 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
         S[m][i] = S0 ? S0[sbase + static_cast<size_t>(16 * m + 4 * gq + i) * DV] : 0.f;
     }
   constexpr bool kOut = MODE == kPassOutputs;
+  constexpr bool kOutHere = kOut && !X::kOn;  // this wavefront forms and stores the outputs
   int e = 0;
   float dn = 1.f, up = 1.f;  // 2^-e, 2^e
   int64_t next_snap = snap_pairs;
@@ -1217,7 +1294,7 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       for (int p = 0; p < NM / 2; ++p) {
         U1 = mma_16x16x32_f16(f.w1[p], sh[p], U1);                // - W1 S0
         U2 = mma_16x16x32_f16(f.w2[p], sh[p], U2);                // - W2 e^g1 S0
-        if constexpr (kOut) {
+        if constexpr (kOutHere) {
           O1 = mma_16x16x32_f16(sh[p], f.q1[p], O1);              // (Qt1 S0)^T
           O2 = mma_16x16x32_f16(sh[p], f.q2[p], O2);              // (Qt2 e^g1 S0)^T
         }
@@ -1272,7 +1349,13 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
       u12[i] = x;
       u12[i + 4] = static_cast<_Float16>(U2[i]);
     }
-    if constexpr (kOut) {
+    if constexpr (X::kOn) {  // the output wavefront's operands, read during the next step
+      uint8_t* xb = xbuf + static_cast<int>(n & 1) * X::kXPair;
+#pragma unroll
+      for (int p = 0; p < NM / 2; ++p) st_at<f16x8>(xb, static_cast<uint32_t>(p * 64 + l) * 16, sh[p]);
+      st_at<f16x8>(xb, static_cast<uint32_t>((NM / 2) * 64 + l) * 16, u12);
+    }
+    if constexpr (kOutHere) {
       O1 = mma_16x16x32_f16(u11, f.m1, O1);                       // + (M1 U1)^T
       O2 = mma_16x16x32_f16(u12, f.m2h, O2);                      // + ([M21 | M2] [U1; U2])^T
       O2 = mma_16x16x32_f16(u12, f.m2l, O2);
@@ -1281,7 +1364,7 @@ __global__ __launch_bounds__(64 * (Ring32Geom<DK, SPW>::kLoaders + SPW)) void kd
     // is the VALU product)
 #pragma unroll
     for (int m = 0; m < NM; ++m) S[m] = mma_16x16x32_f16(f.kb[m], u12, S[m] * f.eg[m]);
-    if constexpr (kOut) {
+    if constexpr (kOutHere) {
       if constexpr (SCALED) {
         O1 *= up;
         O2 *= up;
@@ -1395,7 +1478,8 @@ hipError_t launch_ring32(const ChunkFwdArgs& a, int64_t snap_pairs, hipStream_t 
   int* flags = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) +
                                       static_cast<size_t>(nheads * NPR) * G::kRec);
   hipLaunchKernelGGL((kda_state_pass_ring32<OutT, DK, SPW, SCALED, MODE>),
-                     dim3(static_cast<uint32_t>(blocks)), dim3(64 * (G::kLoaders + SPW)), 0, stream,
+                     dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves), 0, stream,
                      static_cast<const uint16_t*>(a.v), static_cast<const uint8_t*>(a.workspace),
                      a.S0, static_cast<OutT*>(a.o), a.S_T, snap_pairs > 0 ? a.snapshots : nullptr,
                      snap_pairs, a.T, a.H, a.dv, NPR, ngroups, nheads, P, flags, a.E_out);

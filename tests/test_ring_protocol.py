@@ -9,7 +9,11 @@ show directly (a violation would be a race, seen only now and then):
     follows the loader's write of pair n, and the loader does not write the
     slot again before the compute wave's read of pair n is behind a barrier;
   * each loader keeps at most 63 vector loads in flight at a commit (the
-    wait counter's range).
+    wait counter's range);
+  * with the output wavefront (one slice per workgroup, dk = 128), it reads
+    each pair's slot in the same step as the compute wave, and the compute
+    wave's operands for it, left in an exchange buffer by step parity, only
+    after the barrier that ends their write and before they are rewritten.
 
 The constants are read from the kernel source, so a change to the slot or
 loader count is checked here as well. The model follows the kernel's loops
@@ -154,3 +158,68 @@ def test_launcher_instantiates_the_modelled_slice_counts():
     launch = launch[:launch.index("}")]
     found = sorted(int(x) for x in re.findall(r"launch_ring32_pair<OutT, DK, (\d+), MODE>", launch))
     assert found == SPWS
+
+
+def split_constants():
+    text = open(SRC).read()
+    x = text[text.index("struct Ring32Split"):]
+    x = x[:x.index("};")]
+    on = re.search(r"kOn = DK == (\d+) && SPW == (\d+) && MODE == kPassOutputs && !SCALED;", x)
+    nbuf = int(re.search(r"kXStage = kOn \? (\d+) \* kXPair : 0;", x).group(1))
+    per = re.search(r"kXPair = \(DK / (\d+) \+ (\d+)\) \* 1024;", x)
+    dk = int(on.group(1))
+    return dict(dk=dk, spw=int(on.group(2)), buffers=nbuf,
+                pair_bytes=(dk // int(per.group(1)) + int(per.group(2))) * 1024)
+
+
+def simulate_output_wave(T, slots, stages, buffers):
+    """The output wavefront's loop beside the compute wave's: returns its
+    barrier count, the epoch of its read of each pair's slot, and per pair
+    the epochs of the exchange buffer's write (compute wave) and read."""
+    kS = stages
+    NPR = (T + 31) // 32
+    NPS = (NPR + kS - 1) // kS * kS
+    slot_reads, x_reads = {}, {}
+    x_writes = {}                       # buffer -> list of (epoch, pair)
+    for n in range(NPR):                # the compute wave writes pair n in step n
+        x_writes.setdefault(n % buffers, []).append((n + 1, n))
+    barriers = 1
+    epoch = 1
+    for n in range(NPR + 1):
+        if n < NPR:
+            slot_reads[n] = epoch
+        if n > 0:
+            x_reads[n - 1] = epoch
+        if n < NPR:
+            barriers += 1
+            epoch += 1
+    barriers += NPS - NPR
+    return barriers, slot_reads, x_reads, x_writes, NPR
+
+
+def _check_output_wave(T, c, buffers):
+    lb, cb, writes, reads, slot_writes, NPR = simulate(T, c["slots"], c["stages"])
+    ob, slot_reads, x_reads, x_writes, _ = simulate_output_wave(T, c["slots"], c["stages"], buffers)
+    assert ob == lb, "output wavefront barrier count differs at T=%d" % T
+    for n in range(NPR):
+        assert slot_reads[n] == reads[n], "output wavefront reads pair %d in another step" % n
+        wr = [e for e, p in x_writes[n % buffers] if p == n][0]
+        assert wr + 1 <= x_reads[n], "operands of pair %d read before their write completed" % n
+        later = [e for e, p in x_writes[n % buffers] if p > n]
+        if later:
+            assert min(later) >= x_reads[n] + 1, "exchange buffer of pair %d rewritten during its read" % n
+
+
+def test_output_wavefront_barriers_and_exchange_never_race():
+    x = split_constants()
+    c = ring_constants(x["dk"], x["spw"])
+    assert c["slots"] * c["slot_bytes"] + x["buffers"] * x["pair_bytes"] <= 160 * 1024
+    for T in list(range(1, 700)) + [1023, 1024, 1025, 4095, 4096, 4097, 65536, 65537]:
+        _check_output_wave(T, c, x["buffers"])
+
+
+def test_a_single_exchange_buffer_would_race():
+    c = ring_constants(128, 1)
+    with pytest.raises(AssertionError):
+        for T in range(65, 200):
+            _check_output_wave(T, c, 1)

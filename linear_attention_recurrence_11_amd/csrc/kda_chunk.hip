@@ -883,12 +883,24 @@ struct Ring32Geom {
 // those in LDS (two buffers by step parity) and an output wavefront forms and
 // stores pair n's outputs during step n + 1, from the Q~ and M fragments it
 // read from pair n's slot during step n.
+//
+// V on a wavefront of its own (four slices per workgroup, any mode that
+// reads v). With four slices the V loader also loaded every slice's v and
+// wrote its transposed tiles, and it set the pace: 128 heads of 128 x 128 over
+// 8,192 tokens, busy 96% of each step while the other loader waited 81% of
+// it. The V wavefront runs the loaders' loop (same stages, slots and
+// barriers) with the V loads and tiles only, and the two record loaders split
+// the record alone. Two slices keep V on a record loader: a fifth wavefront
+// would halve the registers each may hold (the loaders' loads in flight need
+// more than half of them).
 template <int DK, int SPW, int MODE, bool SCALED>
 struct Ring32Split {
   static constexpr bool kOn = DK == 128 && SPW == 1 && MODE == kPassOutputs && !SCALED;
   static constexpr int kXPair = (DK / 32 + 1) * 1024;  // fp16 state operand + [U1; U2] fragments
   static constexpr int kXStage = kOn ? 2 * kXPair : 0;
-  static constexpr int kWaves = Ring32Geom<DK, SPW>::kLoaders + SPW + (kOn ? 1 : 0);
+  static constexpr bool kVWave = SPW == 4 && MODE != kPassTransition;
+  static constexpr int kVWaveIdx = Ring32Geom<DK, SPW>::kLoaders + SPW;  // after the compute waves
+  static constexpr int kWaves = Ring32Geom<DK, SPW>::kLoaders + SPW + (kOn ? 1 : 0) + (kVWave ? 1 : 0);
 };
 
 // Time per 32-token step of a workgroup serving 2 or 4 slices, relative to one
@@ -996,9 +1008,80 @@ __global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) 
   const int64_t NPS = (NPR + kS - 1) / kS * kS;                // loader steps (and barriers)
 
   constexpr int kLd = G::kLoaders;
+  if constexpr (X::kVWave) {
+    if (wave == X::kVWaveIdx) {
+      // ---------------- V (four slices per workgroup) ----------------
+      // The loaders' loop below (same stages, slots, steps and barriers)
+      // with only its V part: the same loads and transposed tiles as the V
+      // loader's when V shares a record loader.
+      const int va = l & 15, cq = l >> 4;
+      const uint32_t vrow = static_cast<uint32_t>(H * DVV);  // elements per token
+      auto vcol_of = [&](int z) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (MODE == kPassFE) {
+          const int sl = static_cast<int>(group) * SPW + z;
+          return static_cast<uint32_t>(sl >= DK / 16 ? (sl - DK / 16) * 16 + 4 * cq : 4 * cq);
+        } else {
+          return static_cast<uint32_t>((group * SPW + z) * 16 + 4 * cq);
+        }
+      };
+      auto v_on = [&](int z) __attribute__((always_inline)) {
+        return MODE != kPassFE || static_cast<int>(group) * SPW + z >= DK / 16;
+      };
+      const uint16_t* vb = v + hb;
+      Loader32Stage<DK, SPW> st[kS];
+      auto issue = [&](Loader32Stage<DK, SPW>& x, int64_t c) __attribute__((always_inline)) {
+        const int64_t cc = c < NPR ? c : NPR - 1;
+        const int64_t tmax = T - 1 - cc * 32;
+        const uint32_t t0 = static_cast<uint32_t>(2 * va < tmax ? 2 * va : tmax);
+        const uint32_t t1 = static_cast<uint32_t>(2 * va + 1 < tmax ? 2 * va + 1 : tmax);
+        const uint16_t* vp = vb + static_cast<size_t>(cc) * pair_elems;
+#pragma unroll
+        for (int z = 0; z < SPW; ++z) {
+          x.v0[z] = ld_at<u32x2>(vp, (t0 * vrow + vcol_of(z)) * 2u);
+          x.v1[z] = ld_at<u32x2>(vp, (t1 * vrow + vcol_of(z)) * 2u);
+        }
+        x.ok0 = c * 32 + 2 * va < T;
+        x.ok1 = c * 32 + 2 * va + 1 < T;
+      };
+      auto commit = [&](const Loader32Stage<DK, SPW>& x, int64_t c) __attribute__((always_inline)) {
+        uint8_t* dst = ring + static_cast<int>(c % kR) * G::kSlot;
+#pragma unroll
+        for (int z = 0; z < SPW; ++z) {
+          uint8_t* vt = dst + G::kRec + (2 * z + (va >> 3)) * G::kVTile + (va & 7) * 4;
+          const bool k0 = x.ok0 && v_on(z), k1 = x.ok1 && v_on(z);
+          const uint32_t r0[2] = {k0 ? x.v0[z][0] : 0u, k0 ? x.v0[z][1] : 0u};
+          const uint32_t r1[2] = {k1 ? x.v1[z][0] : 0u, k1 ? x.v1[z][1] : 0u};
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const uint32_t b0 = (cc & 1) ? (r0[cc >> 1] >> 16) : (r0[cc >> 1] & 0xffffu);
+            const uint32_t b1 = (cc & 1) ? (r1[cc >> 1] & 0xffff0000u) : (r1[cc >> 1] << 16);
+            *reinterpret_cast<uint32_t*>(vt + (4 * cq + cc) * G::kVPitch) = b0 | b1;
+          }
+        }
+      };
+#pragma unroll
+      for (int c = 0; c < kS; ++c) issue(st[c], c);
+#pragma unroll
+      for (int c = 0; c < kR - 1; ++c) {
+        commit(st[c % kS], c);
+        issue(st[c % kS], c + kS);
+      }
+      ring_barrier();
+      for (int64_t n = 0; n < NPS; n += kS) {
+#pragma unroll
+        for (int k = 0; k < kS; ++k) {
+          const int64_t c = n + k + kR - 1;
+          commit(st[(k + kR - 1) % kS], c);
+          issue(st[(k + kR - 1) % kS], c + kS);
+          ring_barrier();
+        }
+      }
+      return;
+    }
+  }
   if (wave < kLd) {
     // ---------------- loaders ----------------
-    const bool has_v = wave == kLd - 1 && MODE != kPassTransition;
+    const bool has_v = !X::kVWave && wave == kLd - 1 && MODE != kPassTransition;
     // The slice groups of a head read the same record lines in the same
     // step. Each group starts its share of the units at a different place
     // (unit u of this loader's share is taken in turn (u + rot) mod

@@ -121,6 +121,22 @@ def test_transition_and_end_state_match_the_oracle(dt, T, dk, dv):
     assert torch.equal(E, ST)
 
 
+def test_transition_with_four_slices_per_workgroup():
+    """F and E of 64 heads in one pass: 1,024 slices of dk + dv columns, four
+    per workgroup (V then on a wavefront of its own). Each column evolves on
+    its own, so F matches the transition alone (one slice per workgroup) and E
+    the forward's final state (two per workgroup) bit for bit."""
+    B, T, H, dk, dv = 4, 200, 16, 128, 128
+    ins = _mild(inputs.make_forward(B, T, H, dk, dv, "bf16", "zero", seed=77, device=DEV), 0.01)
+    announce("transition, four slices per workgroup", B, T, H)
+    ws = binding.kda_chunk_prep(ins["q"], ins["k"], ins["g"], ins["beta"], dv)
+    F, E = binding.kda_chunk_transition(ws, B, T, H, dk, dv, torch.bfloat16, v=ins["v"], want_E=True)
+    F_only, _ = binding.kda_chunk_transition(ws, B, T, H, dk, dv, torch.bfloat16)
+    _, ST = binding.kda_chunk_state_pass(ins["v"], ws, dk, None)
+    torch.cuda.synchronize()
+    assert torch.equal(F_only, F) and torch.equal(E, ST)
+
+
 def test_transition_of_no_tokens_is_the_identity():
     B, H, dk, dv = 2, 2, 64, 48
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)

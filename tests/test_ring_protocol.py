@@ -10,6 +10,8 @@ show directly (a violation would be a race, seen only now and then):
     slot again before the compute wave's read of pair n is behind a barrier;
   * each loader keeps at most 63 vector loads in flight at a commit (the
     wait counter's range);
+  * the V wavefront (four slices per workgroup) runs the loaders' loop, so
+    the loaders' counts hold for it;
   * with the output wavefront (one slice per workgroup, dk = 128), it reads
     each pair's slot in the same step as the compute wave, and the compute
     wave's operands for it, left in an exchange buffer by step parity, only
@@ -223,3 +225,26 @@ def test_a_single_exchange_buffer_would_race():
     with pytest.raises(AssertionError):
         for T in range(65, 200):
             _check_output_wave(T, c, 1)
+
+
+SKELETON = re.compile(r"for \(int c = 0; c < kS; \+\+c\) issue\(|for \(int c = 0; c < kR - 1; \+\+c\) \{|"
+                      r"commit\(st\[c % kS\], c\);|issue\(st\[c % kS\], c \+ kS\);|ring_barrier\(\);|"
+                      r"for \(int64_t n = 0; n < NPS; n \+= kS\) \{|for \(int k = 0; k < kS; \+\+k\) \{|"
+                      r"const int64_t c = n \+ k \+ kR - 1;|commit\(st\[\(k \+ kR - 1\) % kS\], c\);|"
+                      r"issue\(st\[\(k \+ kR - 1\) % kS\], c \+ kS\);|return;")
+
+
+def _block(text, marker):
+    i = text.index(marker)
+    j = text.index("return;", i)
+    return text[i:j + len("return;")]
+
+
+def test_v_wavefront_runs_the_loaders_loop():
+    # the barrier and slot facts above are modelled on the loaders' loop; the
+    # V wavefront must step through the same prologue, commits, issues and
+    # barriers in the same order
+    text = open(SRC).read()
+    loaders = SKELETON.findall(_block(text, "// ---------------- loaders ----------------"))
+    vwave = SKELETON.findall(_block(text, "// ---------------- V (four slices per workgroup) ----------------"))
+    assert loaders.count("ring_barrier();") == 2 and loaders == vwave

@@ -852,7 +852,8 @@ struct Ring32Geom {
   // workload: 3 slots 1.48-1.51 ms, 4 slots 1.46-1.48, 5 slots 1.50).
   static constexpr int kSlots = 4;
   // loader wavefronts: loader w loads record units j = w, w + kLoaders, ...;
-  // the last one also loads V (two loads per slice). Each has its own load
+  // the last one also loads V (two loads per slice; with four slices a V
+  // wavefront of its own does, see Ring32Split). Each has its own load
   // counter, so each can keep more pairs in flight: kStages - 1 pairs of its
   // loads stay outstanding at each commit, within the 6-bit wait counter (one
   // loader 1.51 ms, two 1.48, three 1.52).
@@ -959,9 +960,11 @@ struct PairFrags {
 
 // With SPW > 1, one workgroup serves SPW consecutive 16-column slices of a
 // head: one compute wavefront per slice, all reading the same record from the
-// shared ring, and the V loader loads every slice's V tiles. A compute unit
-// then advances SPW slices at once, for workloads with more slices than
-// compute units.
+// shared ring, and one wavefront loads every slice's V tiles (the second
+// record loader, or with four slices a V wavefront of its own). A compute
+// unit then advances SPW slices at once, for workloads with more slices than
+// compute units. With one slice (dk = 128, plain output pass) an output
+// wavefront forms and stores the outputs (Ring32Split).
 //
 // flags: one int per (b, h, slice), in the workspace after the records. The
 // plain pass (SCALED = false) writes every slice's flag; the scaled pass

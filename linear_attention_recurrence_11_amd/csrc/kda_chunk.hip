@@ -1015,50 +1015,70 @@ __global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) 
     if (wave == X::kVWaveIdx) {
       // ---------------- V (four slices per workgroup) ----------------
       // The loaders' loop below (same stages, slots, steps and barriers)
-      // with only its V part: the same loads and transposed tiles as the V
-      // loader's when V shares a record loader.
-      const int va = l & 15, cq = l >> 4;
+      // with only a V part. Load i (i = 0..3) of a pair covers whole 128-byte
+      // rows: lane l takes 16 bytes, columns 8j .. 8j + 7 (j = l & 7) of the
+      // group's 64, of token 8i + (l >> 3), so each token costs one request
+      // instead of one per slice. The lanes of tokens t and t ^ 1 (l and l ^ 8,
+      // a DPP rotation by 8 within a row) swap their pieces; the even token's
+      // lane then writes columns 0..3 of its piece and the odd token's lane
+      // columns 4..7, one dword (two bf16, even token low) per column, into
+      // the same V^T tiles as the loader's form.
+      static_assert(SPW == 4 && (DK / 16) % SPW == 0, "a group of four slices is all F or all E");
+      const int j = l & 7, zs = j >> 1, tl = l >> 3;
+      const bool odd = (tl & 1) != 0;
       const uint32_t vrow = static_cast<uint32_t>(H * DVV);  // elements per token
-      auto vcol_of = [&](int z) __attribute__((always_inline)) -> uint32_t {
-        if constexpr (MODE == kPassFE) {
-          const int sl = static_cast<int>(group) * SPW + z;
-          return static_cast<uint32_t>(sl >= DK / 16 ? (sl - DK / 16) * 16 + 4 * cq : 4 * cq);
-        } else {
-          return static_cast<uint32_t>((group * SPW + z) * 16 + 4 * cq);
-        }
-      };
-      auto v_on = [&](int z) __attribute__((always_inline)) {
-        return MODE != kPassFE || static_cast<int>(group) * SPW + z >= DK / 16;
-      };
+      // kPassFE: a group's slices are all F (v = 0: the loads read column
+      // 8j and are zeroed at commit) or all E, at column (s - dk / 16) * 16
+      const int sl0 = static_cast<int>(group) * SPW;
+      const bool von = MODE != kPassFE || sl0 >= DK / 16;
+      const uint32_t col = static_cast<uint32_t>(
+          (MODE == kPassFE ? (von ? (sl0 - DK / 16) * 16 : 0) : sl0 * 16) + 8 * j);
       const uint16_t* vb = v + hb;
-      Loader32Stage<DK, SPW> st[kS];
-      auto issue = [&](Loader32Stage<DK, SPW>& x, int64_t c) __attribute__((always_inline)) {
+      struct VRows {
+        u32x4 x[4];
+        bool ok[4];
+      };
+      VRows st[kS];
+      auto issue = [&](VRows& x, int64_t c) __attribute__((always_inline)) {
         const int64_t cc = c < NPR ? c : NPR - 1;
         const int64_t tmax = T - 1 - cc * 32;
-        const uint32_t t0 = static_cast<uint32_t>(2 * va < tmax ? 2 * va : tmax);
-        const uint32_t t1 = static_cast<uint32_t>(2 * va + 1 < tmax ? 2 * va + 1 : tmax);
         const uint16_t* vp = vb + static_cast<size_t>(cc) * pair_elems;
 #pragma unroll
-        for (int z = 0; z < SPW; ++z) {
-          x.v0[z] = ld_at<u32x2>(vp, (t0 * vrow + vcol_of(z)) * 2u);
-          x.v1[z] = ld_at<u32x2>(vp, (t1 * vrow + vcol_of(z)) * 2u);
+        for (int i = 0; i < 4; ++i) {
+          const int t = 8 * i + tl;
+          const uint32_t tt = static_cast<uint32_t>(t < tmax ? t : tmax);
+          x.x[i] = ld_at<u32x4>(vp, (tt * vrow + col) * 2u);
+          x.ok[i] = c * 32 + t < T;
         }
-        x.ok0 = c * 32 + 2 * va < T;
-        x.ok1 = c * 32 + 2 * va + 1 < T;
       };
-      auto commit = [&](const Loader32Stage<DK, SPW>& x, int64_t c) __attribute__((always_inline)) {
+      auto commit = [&](const VRows& x, int64_t c) __attribute__((always_inline)) {
         uint8_t* dst = ring + static_cast<int>(c % kR) * G::kSlot;
 #pragma unroll
-        for (int z = 0; z < SPW; ++z) {
-          uint8_t* vt = dst + G::kRec + (2 * z + (va >> 3)) * G::kVTile + (va & 7) * 4;
-          const bool k0 = x.ok0 && v_on(z), k1 = x.ok1 && v_on(z);
-          const uint32_t r0[2] = {k0 ? x.v0[z][0] : 0u, k0 ? x.v0[z][1] : 0u};
-          const uint32_t r1[2] = {k1 ? x.v1[z][0] : 0u, k1 ? x.v1[z][1] : 0u};
+        for (int i = 0; i < 4; ++i) {
+          const int t = 8 * i + tl;  // chunk t >> 4, token pair (t & 15) >> 1
+          const bool keep = x.ok[i] && von;
+          // dword d of a piece holds columns 2d (low) and 2d + 1 (high); the
+          // even token's lane needs the odd one's dwords 0, 1 and sends its
+          // dwords 2, 3, and the other way round
+          uint32_t mine[4], recv[2];
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const uint32_t b0 = (cc & 1) ? (r0[cc >> 1] >> 16) : (r0[cc >> 1] & 0xffffu);
-            const uint32_t b1 = (cc & 1) ? (r1[cc >> 1] & 0xffff0000u) : (r1[cc >> 1] << 16);
-            *reinterpret_cast<uint32_t*>(vt + (4 * cq + cc) * G::kVPitch) = b0 | b1;
+          for (int d = 0; d < 4; ++d) mine[d] = keep ? x.x[i][d] : 0u;
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t send = odd ? mine[d] : mine[2 + d];
+            recv[d] = static_cast<uint32_t>(
+                __builtin_amdgcn_update_dpp(0, static_cast<int>(send), 0x128, 0xf, 0xf, false));
+          }
+          uint8_t* vt = dst + G::kRec + (2 * zs + (t >> 4)) * G::kVTile + ((t & 15) >> 1) * 4;
+          const int c0 = 8 * (j & 1) + (odd ? 4 : 0);  // first column of the four this lane writes
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int d = k >> 1;
+            const uint32_t ew = odd ? recv[d] : mine[d];      // even token, this column pair
+            const uint32_t ow = odd ? mine[2 + d] : recv[d];  // odd token
+            const uint32_t e = (k & 1) ? (ew >> 16) : (ew & 0xffffu);
+            const uint32_t o2 = (k & 1) ? (ow & 0xffff0000u) : (ow << 16);
+            *reinterpret_cast<uint32_t*>(vt + (c0 + k) * G::kVPitch) = e | o2;
           }
         }
       };

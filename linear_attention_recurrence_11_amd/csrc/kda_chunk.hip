@@ -910,8 +910,85 @@ struct Ring32Split {
 constexpr double kSpw2StepCost = 1.12;
 constexpr double kSpw4StepCost = 1.38;
 
+
+// Whole-row V loads (two or four slices per workgroup). A token's columns
+// of the group's slices are contiguous in v (64 or 128 bytes), so each load
+// gives every lane 16 bytes (8 columns, piece j) of one token and covers
+// whole rows: one request per token instead of one per slice. The lanes of
+// tokens t and t ^ 1 are l and l ^ 8 (a DPP rotation by 8 within a 16-lane
+// row); they swap half their pieces, and each writes four dwords (even token
+// low, odd token high) of the transposed tiles: the even token's lane columns
+// 0..3 of the piece, the odd token's lane columns 4..7.
+template <int SPW>
+struct VRows {
+  static_assert(SPW == 2 || SPW == 4, "whole rows of two or four slices");
+  static constexpr int kLoads = SPW;  // loads per pair and lane (32 tokens / (64 / (2 * SPW)))
+  u32x4 x[kLoads];
+  bool ok[kLoads];
+  // piece (8 columns) and token (of the pair) of lane l in load i
+  __device__ static int piece(int l) { return SPW == 4 ? (l & 7) : (l & 3); }
+  __device__ static int token(int l, int i) {
+    return SPW == 4 ? 8 * i + (l >> 3)
+                    : 16 * i + (((l >> 3) & 1) | (((l >> 2) & 1) << 1) | ((l >> 4) << 2));
+  }
+};
+
+template <int SPW>
+struct VRowsSlot {};
+template <>
+struct VRowsSlot<2> {
+  VRows<2> vr;
+};
+
+// Loads of pair c (tokens past T read the last token and are zeroed at
+// commit); vp points at the pair's first token row, col at the lane's piece.
+template <int SPW>
+__device__ __forceinline__ void vrows_issue(VRows<SPW>& x, const uint16_t* vp, uint32_t vrow, uint32_t col,
+                                            int64_t tmax, int64_t t0, int64_t T, int l) {
+#pragma unroll
+  for (int i = 0; i < VRows<SPW>::kLoads; ++i) {
+    const int t = VRows<SPW>::token(l, i);
+    const uint32_t tt = static_cast<uint32_t>(t < tmax ? t : tmax);
+    x.x[i] = ld_at<u32x4>(vp, (tt * vrow + col) * 2u);
+    x.ok[i] = t0 + t < T;
+  }
+}
+
+// The transposed tiles of a pair: vt0 is the slot's first tile (slice 0,
+// chunk 0); tile 2z + chunk holds column rows of kVPitch bytes.
+template <int SPW, int kVPitch, int kVTile>
+__device__ __forceinline__ void vrows_commit(const VRows<SPW>& x, uint8_t* vt0, bool von, int l) {
+  const int j = VRows<SPW>::piece(l);
+  const bool odd = ((l >> 3) & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < VRows<SPW>::kLoads; ++i) {
+    const int t = VRows<SPW>::token(l, i);  // chunk t >> 4, token pair (t & 15) >> 1
+    const bool keep = x.ok[i] && von;
+    // dword d of a piece holds columns 2d (low) and 2d + 1 (high); the even
+    // token's lane needs the odd one's dwords 0, 1 and sends its dwords 2, 3
+    // (scalars, not arrays: a select between array elements becomes an
+    // indexed load from scratch)
+    const uint32_t m0 = keep ? x.x[i][0] : 0u, m1 = keep ? x.x[i][1] : 0u;
+    const uint32_t m2 = keep ? x.x[i][2] : 0u, m3 = keep ? x.x[i][3] : 0u;
+    const uint32_t r0 = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? m0 : m2), 0x128, 0xf, 0xf, false));
+    const uint32_t r1 = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(odd ? m1 : m3), 0x128, 0xf, 0xf, false));
+    uint8_t* vt = vt0 + (2 * (j >> 1) + (t >> 4)) * kVTile + ((t & 15) >> 1) * 4;
+    const int c0 = 8 * (j & 1) + (odd ? 4 : 0);  // first column of the four this lane writes
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t ew = odd ? (k < 2 ? r0 : r1) : (k < 2 ? m0 : m1);  // even token, this column pair
+      const uint32_t ow = odd ? (k < 2 ? m2 : m3) : (k < 2 ? r0 : r1);  // odd token
+      const uint32_t e = (k & 1) ? (ew >> 16) : (ew & 0xffffu);
+      const uint32_t o2 = (k & 1) ? (ow & 0xffff0000u) : (ow << 16);
+      *reinterpret_cast<uint32_t*>(vt + (c0 + k) * kVPitch) = e | o2;
+    }
+  }
+}
+
 template <int DK, int SPW>
-struct Loader32Stage {
+struct Loader32Stage : VRowsSlot<SPW> {  // two slices: V in whole rows (vr)
   u32x4 r[Ring32Geom<DK, SPW>::kUnitsPer];
   u32x2 v0[SPW], v1[SPW];  // tokens 2a and 2a + 1, four columns of each slice (bf16)
   bool ok0, ok1;
@@ -1015,72 +1092,23 @@ __global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) 
     if (wave == X::kVWaveIdx) {
       // ---------------- V (four slices per workgroup) ----------------
       // The loaders' loop below (same stages, slots, steps and barriers)
-      // with only a V part. Load i (i = 0..3) of a pair covers whole 128-byte
-      // rows: lane l takes 16 bytes, columns 8j .. 8j + 7 (j = l & 7) of the
-      // group's 64, of token 8i + (l >> 3), so each token costs one request
-      // instead of one per slice. The lanes of tokens t and t ^ 1 (l and l ^ 8,
-      // a DPP rotation by 8 within a row) swap their pieces; the even token's
-      // lane then writes columns 0..3 of its piece and the odd token's lane
-      // columns 4..7, one dword (two bf16, even token low) per column, into
-      // the same V^T tiles as the loader's form.
+      // with only a V part, in whole rows (VRows).
       static_assert(SPW == 4 && (DK / 16) % SPW == 0, "a group of four slices is all F or all E");
-      const int j = l & 7, zs = j >> 1, tl = l >> 3;
-      const bool odd = (tl & 1) != 0;
       const uint32_t vrow = static_cast<uint32_t>(H * DVV);  // elements per token
-      // kPassFE: a group's slices are all F (v = 0: the loads read column
-      // 8j and are zeroed at commit) or all E, at column (s - dk / 16) * 16
+      // kPassFE: a group's slices are all F (v = 0: the loads read columns
+      // 8j .. and are zeroed at commit) or all E, at column (s - dk / 16) * 16
       const int sl0 = static_cast<int>(group) * SPW;
       const bool von = MODE != kPassFE || sl0 >= DK / 16;
       const uint32_t col = static_cast<uint32_t>(
-          (MODE == kPassFE ? (von ? (sl0 - DK / 16) * 16 : 0) : sl0 * 16) + 8 * j);
+          (MODE == kPassFE ? (von ? (sl0 - DK / 16) * 16 : 0) : sl0 * 16) + 8 * VRows<SPW>::piece(l));
       const uint16_t* vb = v + hb;
-      struct VRows {
-        u32x4 x[4];
-        bool ok[4];
-      };
-      VRows st[kS];
-      auto issue = [&](VRows& x, int64_t c) __attribute__((always_inline)) {
+      VRows<SPW> st[kS];
+      auto issue = [&](VRows<SPW>& x, int64_t c) __attribute__((always_inline)) {
         const int64_t cc = c < NPR ? c : NPR - 1;
-        const int64_t tmax = T - 1 - cc * 32;
-        const uint16_t* vp = vb + static_cast<size_t>(cc) * pair_elems;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 8 * i + tl;
-          const uint32_t tt = static_cast<uint32_t>(t < tmax ? t : tmax);
-          x.x[i] = ld_at<u32x4>(vp, (tt * vrow + col) * 2u);
-          x.ok[i] = c * 32 + t < T;
-        }
+        vrows_issue<SPW>(x, vb + static_cast<size_t>(cc) * pair_elems, vrow, col, T - 1 - cc * 32, c * 32, T, l);
       };
-      auto commit = [&](const VRows& x, int64_t c) __attribute__((always_inline)) {
-        uint8_t* dst = ring + static_cast<int>(c % kR) * G::kSlot;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 8 * i + tl;  // chunk t >> 4, token pair (t & 15) >> 1
-          const bool keep = x.ok[i] && von;
-          // dword d of a piece holds columns 2d (low) and 2d + 1 (high); the
-          // even token's lane needs the odd one's dwords 0, 1 and sends its
-          // dwords 2, 3, and the other way round
-          uint32_t mine[4], recv[2];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) mine[d] = keep ? x.x[i][d] : 0u;
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const uint32_t send = odd ? mine[d] : mine[2 + d];
-            recv[d] = static_cast<uint32_t>(
-                __builtin_amdgcn_update_dpp(0, static_cast<int>(send), 0x128, 0xf, 0xf, false));
-          }
-          uint8_t* vt = dst + G::kRec + (2 * zs + (t >> 4)) * G::kVTile + ((t & 15) >> 1) * 4;
-          const int c0 = 8 * (j & 1) + (odd ? 4 : 0);  // first column of the four this lane writes
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int d = k >> 1;
-            const uint32_t ew = odd ? recv[d] : mine[d];      // even token, this column pair
-            const uint32_t ow = odd ? mine[2 + d] : recv[d];  // odd token
-            const uint32_t e = (k & 1) ? (ew >> 16) : (ew & 0xffffu);
-            const uint32_t o2 = (k & 1) ? (ow & 0xffff0000u) : (ow << 16);
-            *reinterpret_cast<uint32_t*>(vt + (c0 + k) * G::kVPitch) = e | o2;
-          }
-        }
+      auto commit = [&](const VRows<SPW>& x, int64_t c) __attribute__((always_inline)) {
+        vrows_commit<SPW, G::kVPitch, G::kVTile>(x, ring + static_cast<int>(c % kR) * G::kSlot + G::kRec, von, l);
       };
 #pragma unroll
       for (int c = 0; c < kS; ++c) issue(st[c], c);
@@ -1132,6 +1160,15 @@ __global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) 
       return MODE != kPassFE || static_cast<int>(group) * SPW + z >= DK / 16;
     };
     const uint16_t* vb = v + hb;
+    // two slices: whole rows (VRows); F or E for the whole group in kPassFE
+    auto von2 = [&]() __attribute__((always_inline)) {
+      return MODE != kPassFE || static_cast<int>(group) * SPW >= DK / 16;
+    };
+    auto col2 = [&]() __attribute__((always_inline)) {
+      const int sl0 = static_cast<int>(group) * SPW;
+      return static_cast<uint32_t>((MODE == kPassFE ? (von2() ? (sl0 - DK / 16) * 16 : 0) : sl0 * 16) +
+                                   8 * VRows<2>::piece(l));
+    };
     // Loads are unconditional (pairs past the end re-read the last one; V
     // tokens past T read the last token and are zeroed at commit): a branch
     // around them would make the compiler's wait counting conservative.
@@ -1143,7 +1180,11 @@ __global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) 
         const int j = wave + (u + rot) % G::kUnitsPer * kLd;
         st.r[u] = ld_at<u32x4>(src, static_cast<uint32_t>(j * 64 + l) * 16);
       }
-      if (has_v) {
+      if constexpr (SPW == 2) {
+        if (has_v)
+          vrows_issue<2>(st.vr, vb + static_cast<size_t>(cc) * pair_elems, vrow, col2(), T - 1 - cc * 32,
+                         c * 32, T, l);
+      } else if (has_v) {
         const int64_t tmax = T - 1 - cc * 32;
         const uint32_t t0 = static_cast<uint32_t>(2 * va < tmax ? 2 * va : tmax);
         const uint32_t t1 = static_cast<uint32_t>(2 * va + 1 < tmax ? 2 * va + 1 : tmax);
@@ -1166,7 +1207,9 @@ __global__ __launch_bounds__((64 * Ring32Split<DK, SPW, MODE, SCALED>::kWaves)) 
         const int j = wave + (u + rot) % G::kUnitsPer * kLd;
         st_at<u32x4>(dst, static_cast<uint32_t>(j * 64 + l) * 16, st.r[u]);
       }
-      if (has_v) {
+      if constexpr (SPW == 2) {
+        if (has_v) vrows_commit<2, G::kVPitch, G::kVTile>(st.vr, dst + G::kRec, von2(), l);
+      } else if (has_v) {
         // V^T[col][token], the exact bf16 values, one tile per chunk of the
         // pair (rows of G::kVPitch bytes), two tiles per slice: the compute
         // lane (c16, gq) reads tokens 4gq .. 4gq+3 of column c16. This lane

@@ -121,14 +121,16 @@ def test_transition_and_end_state_match_the_oracle(dt, T, dk, dv):
     assert torch.equal(E, ST)
 
 
-def test_transition_with_four_slices_per_workgroup():
-    """F and E of 64 heads in one pass: 1,024 slices of dk + dv columns, four
-    per workgroup (V then on a wavefront of its own). Each column evolves on
-    its own, so F matches the transition alone (one slice per workgroup) and E
-    the forward's final state (two per workgroup) bit for bit."""
-    B, T, H, dk, dv = 4, 200, 16, 128, 128
-    ins = _mild(inputs.make_forward(B, T, H, dk, dv, "bf16", "zero", seed=77, device=DEV), 0.01)
-    announce("transition, four slices per workgroup", B, T, H)
+@pytest.mark.parametrize("B", [2, 4], ids=["two_slices", "four_slices"])
+def test_transition_with_several_slices_per_workgroup(B):
+    """F and E of 32 or 64 heads in one pass: 512 or 1,024 slices of dk + dv
+    columns, two or four per workgroup (V in whole rows, on the second loader
+    or on a wavefront of its own). Each column evolves on its own, so F
+    matches the transition alone (one slice per workgroup) and E the forward's
+    final state bit for bit."""
+    T, H, dk, dv = 200, 16, 128, 128
+    ins = _mild(inputs.make_forward(B, T, H, dk, dv, "bf16", "zero", seed=77 + B, device=DEV), 0.01)
+    announce("transition, several slices per workgroup", B, T, H)
     ws = binding.kda_chunk_prep(ins["q"], ins["k"], ins["g"], ins["beta"], dv)
     F, E = binding.kda_chunk_transition(ws, B, T, H, dk, dv, torch.bfloat16, v=ins["v"], want_E=True)
     F_only, _ = binding.kda_chunk_transition(ws, B, T, H, dk, dv, torch.bfloat16)
